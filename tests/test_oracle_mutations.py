@@ -1,0 +1,71 @@
+"""The oracle's pins must catch plausible mistakes planted in the oracle (CPU only).
+
+Each mutation edits one expression of the oracle's source text, loads the edited copy as
+a throw-away module and runs it against the pins of tests/test_oracle_attention.py and
+tests/test_oracle_positions.py (brute force, library causal attention, golden G values).
+A mutation that no pin notices would mean the pins leave that part of the oracle open.
+"""
+import os
+import types
+
+import numpy as np
+import pytest
+
+from tests.test_oracle_attention import _rand, brute_force, rope_complex, sdpa_causal
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "bifocal_oracle.py")
+
+MUTATIONS = [
+    ("rotation sign", "x1 * c - x2 * s", "x1 * c + x2 * s"),
+    ("rotation transposed", "x1 * s + x2 * c", "x2 * s + x1 * c"),
+    ("window boundary off by one", "        local = (rel >= 0) & (rel < w0)", "        local = (rel >= 0) & (rel <= w0)"),
+    ("remote boundary off by one", "        remote = rel >= w0", "        remote = rel > w0"),
+    ("floor instead of ceil in G", "return max(1, -(-L // w_pretrained))", "return max(1, L // w_pretrained)"),
+    ("dropped query correction", "q_rem = _remote_vectors(q, L, G, theta)\n    k_rem = _remote_vectors(k, L, G, theta)\n    group = Hq // Hkv\n    scale",
+     "q_rem = q\n    k_rem = _remote_vectors(k, L, G, theta)\n    group = Hq // Hkv\n    scale"),
+    ("correction sign", "return x // int(G) - x", "return x - x // int(G)"),
+    ("frequency exponent", "-2.0 * k / head_dim", "-1.0 * k / head_dim"),
+    ("score scale", "scale = 1.0 / math.sqrt(D)\n    out = np.zeros((B, rows.size", "scale = 1.0 / D\n    out = np.zeros((B, rows.size"),
+    ("GQA mapping", "kv = h // group\n                s_base", "kv = h % Hkv\n                s_base"),
+    ("lse drops the max", "lse[b, h, start:start + r.size] = (m + np.log(l))[:, 0]",
+     "lse[b, h, start:start + r.size] = np.log(l)[:, 0]"),
+]
+
+
+def _load_mutant(old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(text.replace(old, new), SRC + "<mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+def _pins_pass(m) -> bool:
+    """True if the (possibly mutated) oracle passes a compact set of the pins."""
+    try:
+        # Golden G values (review page, Validation/Significance; atlas summary, Approach).
+        if m.group_size(131072, 32768) != 4 or m.group_size(32769, 32768) != 2 or m.group_size(8, 32768) != 1:
+            return False
+        for L, D, Hq, Hkv, wp, w0, theta in [(30, 8, 4, 2, 8, 5, 1e4), (26, 8, 2, 1, 9, 0, 1e4)]:
+            qr, kr, v = _rand(50 + L, 1, L, Hq, Hkv, D)
+            pos = np.arange(L)
+            q, k = rope_complex(qr, pos, theta), rope_complex(kr, pos, theta)
+            want_o, want_lse = brute_force(qr, kr, v, w0, wp, theta)
+            o, lse = m.bifocal_attention(q, k, v, w0=w0, w_pretrained=wp, theta=theta)
+            if not (np.allclose(o, want_o, atol=1e-9, rtol=0) and np.allclose(lse, want_lse, atol=1e-9, rtol=0)):
+                return False
+        # G = 1 against library causal attention.
+        q, k, v = _rand(60, 1, 40, 4, 2, 16)
+        o, _ = m.bifocal_attention(q, k, v, w0=8, w_pretrained=64, theta=1e4)
+        return bool(np.allclose(o, sdpa_causal(q, k, v), atol=1e-9, rtol=0))
+    except Exception:
+        return False
+
+
+def test_unmutated_oracle_passes_compact_pins():
+    assert _pins_pass(_load_mutant("import math", "import math"))
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new):
+    assert not _pins_pass(_load_mutant(old, new)), f"pins did not catch: {name}"
