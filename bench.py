@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the bifocal attention hot path on one MI355X.
+
+One step = one fused bifocal prefill of the Qwen3-8B layer shape at L = 131072
+(32 query / 8 KV heads, D = 128, w_pretrained = 32768 so G = 4, w0 = 2048) followed by the
+512-step single-token decode of the same heads from 98001 to 98512 cached keys (G goes
+3 -> 4 at L = 98305). Inputs are seeded synthetic bf16 N(0, 1) draws, resident in HBM
+before timing starts.
+
+Prints ONE JSON line. `value` is the prefill throughput in TFLOP/s with the algorithmic
+flop count 4 * Hq * D * L(L+1)/2 (one score and one PV product per causal pair); the
+decode KV-cache bandwidth (4096 * L bytes per step) is reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time for the baseline sample")
+    ap.add_argument("--prefill-only", action="store_true", help="skip the decode leg (profiling runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the bifocal kernels have no multi-GPU path "
+              "(sharding is by KV head or key range, described in the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from zero_shot_rope_amd import bifocal as Z
+    from zero_shot_rope_amd import workloads as W
+
+    Z.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    pcfg, dcfg = W.QWEN3_8B_128K, W.QWEN3_8B_DECODE
+    t0 = time.time()
+    pb = W.prefill_inputs(pcfg)
+    to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to_dev(pb["q"]), to_dev(pb["k"]), to_dev(pb["v"])
+    o = torch.empty_like(q)
+    log(f"prefill inputs {tuple(q.shape)} ready in {time.time() - t0:.1f}s")
+    if not args.prefill_only:
+        db = W.decode_inputs(dcfg)
+        kc, vc, qs = to_dev(db["k_cache"]), to_dev(db["v_cache"]), to_dev(db["q_steps"])
+        od = torch.empty((dcfg.batch, dcfg.n_q_heads, dcfg.head_dim), dtype=torch.bfloat16, device=dev)
+        ws_bytes = Z.bifocal_decode_workspace_bytes(dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
+                                                    dcfg.capacity)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        log(f"decode cache {tuple(kc.shape)} ready")
+    sptr = stream.cuda_stream
+
+    def prefill(w0):
+        Z.bifocal_prefill(q, k, v, o, None, pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim, pcfg.L, w0,
+                          pcfg.w_pretrained, pcfg.rope_theta, sptr)
+
+    def decode_steps():
+        for t in range(dcfg.steps):
+            L = dcfg.L_first + t
+            Z.bifocal_decode(qs[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, L,
+                             dcfg.capacity, dcfg.w0, dcfg.w_pretrained, dcfg.rope_theta, ws, ws_bytes, sptr)
+
+    def step(ev):
+        ev[0].record(stream)
+        prefill(pcfg.w0)
+        ev[1].record(stream)
+        if not args.prefill_only:
+            decode_steps()
+        ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w_start
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    log(f"timed {args.steps} steps: prefill ms {['%.2f' % x for x in pre_ms]} decode ms {['%.2f' % x for x in dec_ms]}")
+
+    flops = pcfg.flops()
+    pre_avg = float(np.mean(pre_ms))
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+
+    # Per-step decode timing (events around each call) for the G = 3 and G = 4 halves.
+    decode = None
+    if not args.prefill_only:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(dcfg.steps + 1)]
+        ev[0].record(stream)
+        for t in range(dcfg.steps):
+            L = dcfg.L_first + t
+            Z.bifocal_decode(qs[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, L,
+                             dcfg.capacity, dcfg.w0, dcfg.w_pretrained, dcfg.rope_theta, ws, ws_bytes, sptr)
+            ev[t + 1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([ev[t].elapsed_time(ev[t + 1]) for t in range(dcfg.steps)])  # ms
+        Ls = dcfg.L_first + np.arange(dcfg.steps)
+        byts = np.array([dcfg.bytes_per_step(L) for L in Ls])
+        gbps = byts / (per * 1e-3) / 1e9
+        flip = Ls > 3 * pcfg.w_pretrained
+        total_bytes = float(byts.sum())
+        dec_avg = float(np.mean(dec_ms))
+        dec_gbps = total_bytes / (dec_avg * 1e-3) / 1e9
+        decode = {
+            "value": round(dec_gbps, 1), "unit": "GB/s", "steps_per_call": dcfg.steps,
+            "ms_per_512_steps": round(dec_avg, 3), "us_per_step_median": round(float(np.median(per)) * 1e3, 2),
+            "GBps_median_G3": round(float(np.median(gbps[~flip])), 1),
+            "GBps_median_G4": round(float(np.median(gbps[flip])), 1),
+            "GBps_min": round(float(gbps.min()), 1),
+            "bytes_per_step": "4096 * L (K and V rows of 8 KV heads x 128 dims, bf16, read once)",
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        }
+
+    # Matched control: the same kernel with every pair local (plain causal RoPE attention).
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    prefill(pcfg.L)
+    cev[0].record(stream)
+    prefill(pcfg.L)
+    cev[1].record(stream)
+    prefill(pcfg.L)
+    cev[2].record(stream)
+    torch.cuda.synchronize()
+    ctrl_ms = (cev[0].elapsed_time(cev[1]) + cev[1].elapsed_time(cev[2])) / 2.0
+    ctrl_tflops = flops / (ctrl_ms * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(pb, pcfg, args.cpu_seconds)
+
+    step_ms = wall * 1e3 / args.steps
+    out = {
+        "metric": "bifocal prefill TFLOP/s at 128K (Qwen3-8B heads); decode KV-cache GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. N(0,1), bf16-rounded)",
+        "config": {
+            "workload": "qwen3_8b_L131072 fused bifocal prefill + qwen3_8b_decode_98k 512 decode steps",
+            "batch": pcfg.batch, "n_q_heads": pcfg.n_q_heads, "n_kv_heads": pcfg.n_kv_heads,
+            "head_dim": pcfg.head_dim, "L": pcfg.L, "w0": pcfg.w0, "w_pretrained": pcfg.w_pretrained,
+            "rope_theta": pcfg.rope_theta, "G": 4, "decode_L": [dcfg.L_first, dcfg.L_first + dcfg.steps - 1],
+            "parallelism": "single GPU",
+        },
+        "prefill_ms": round(pre_avg, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<128>", "flops_per_launch": flops},
+        "matched_control": {"what": "same kernel, w0 >= L (plain causal RoPE attention)",
+                            "ms": round(ctrl_ms, 3), "TFLOP/s": round(ctrl_tflops, 2),
+                            "bifocal_over_control": round(ctrl_ms / pre_avg, 4)},
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(pb, pcfg, target_s):
+    """Time the fp64 oracle on a bounded sample of the same prefill workload (rank 0, N = 1)."""
+    from oracle import bifocal_attention
+    from zero_shot_rope_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    qf = W.bf16_bits_to_float32(pb["q"])
+    kf = W.bf16_bits_to_float32(pb["k"])
+    vf = W.bf16_bits_to_float32(pb["v"])
+    L = pcfg.L
+    # Rows from the end of the sequence (the longest causal rows), one block per timing unit.
+    rows_all = np.arange(L - 1, -1, -97)
+    done_rows = []
+    t0 = time.perf_counter()
+    n = 2
+    while True:
+        rows = rows_all[len(done_rows):len(done_rows) + n]
+        bifocal_attention(qf, kf, vf, w0=pcfg.w0, w_pretrained=pcfg.w_pretrained, theta=pcfg.rope_theta,
+                          rows=np.sort(rows), block=64)
+        done_rows.extend(rows.tolist())
+        el = time.perf_counter() - t0
+        if el >= target_s or len(done_rows) >= 256:
+            break
+        per_row = el / len(done_rows)
+        n = max(1, min(64, int((target_s - el) / per_row)))
+    el = time.perf_counter() - t0
+    flop = sum(4.0 * pcfg.n_q_heads * pcfg.head_dim * (int(i) + 1) for i in done_rows)
+    log(f"cpu oracle: {len(done_rows)} rows in {el:.1f}s")
+    return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done_rows)} query rows (every 97th from row {L - 1} down, all 32 heads) of the "
+                      f"128K prefill, fp64 numpy; {el:.1f} s including K/V conversion and rotation"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,110 @@
+/*
+ * bifocal.h -- C ABI of the MI355X (gfx950) Dynamic Bifocal RoPE attention library.
+ *
+ * The method (Jet-Long, "Efficient Long-Context Extension with Dynamic Bifocal RoPE"):
+ * causal grouped-query attention in which a query/key pair (i, j), j <= i, is
+ *   - LOCAL  when 0 <= i - j < w0: scored with the ordinary RoPE positions i and j;
+ *   - REMOTE when i - j >= w0:     scored as if the positions were f(i) and f(j),
+ *     f(x) = floor(x / G), G = max(1, ceil(L / w_pretrained)) from the current length L.
+ * Sources: review page "Paper Review -- Jet-Long" (romaanj.github.io), section Method;
+ * gist.science technical summary "Technische Samenvatting: Jet-Long", Methodologie
+ * sections 1 (G and f) and 2 (correction rotation, inclusion-exclusion merge).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (HIP), row-major, no padding.
+ *   - Element type is bfloat16 (raw 16-bit storage) for Q, K, V, O; LSE is float32.
+ *   - q and k are POST-base-RoPE: each vector is already rotated at its absolute position
+ *     (the cache convention of the method: cached keys stay at their base positions and
+ *     are never rewritten). The library applies only the correction rotation by
+ *     Delta_x = f(x) - x to remote vectors, in registers.
+ *   - RoPE pairs are half-split, (d, d + D/2), with frequencies theta^(-2k/D).
+ *   - Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *   - Softmax scale is 1/sqrt(head_dim). LSE outputs are natural-log log-sum-exps.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ *     The library allocates nothing, keeps no state between calls, never synchronises
+ *     the host, and is safe to call from several host threads.
+ *   - Every argument is validated on the host BEFORE any HIP call; a failed check
+ *     returns a negative status and leaves device memory untouched. C++ exceptions never
+ *     cross this boundary. A failed kernel launch returns BIFOCAL_EHIP.
+ *   - Ownership: the caller owns every buffer; pointers are only used during the call's
+ *     kernels. Input buffers are never written.
+ */
+#ifndef BIFOCAL_H_
+#define BIFOCAL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BIFOCAL_OK = 0,
+  BIFOCAL_EINVAL = -1,       /* null pointer, non-positive size, bad w0/theta, head mismatch */
+  BIFOCAL_EUNSUPPORTED = -2, /* valid arguments the kernels do not implement (head_dim, group) */
+  BIFOCAL_EWORKSPACE = -3,   /* decode workspace missing or smaller than required */
+  BIFOCAL_EHIP = -4          /* a HIP runtime call or kernel launch failed */
+} bifocal_status;
+
+/* Dynamic group size G = max(1, ceil(L / w_pretrained)) (review page, Method; gist.science
+ * summary, Methodologie section 1). Pure host arithmetic in int64.
+ * Returns G >= 1, or BIFOCAL_EINVAL (< 0) when L < 1 or w_pretrained < 1. */
+int64_t bifocal_group_size(int64_t L, int64_t w_pretrained);
+
+/* Fused bifocal prefill (one kernel launch).
+ *   q    [batch, L, n_q_heads,  head_dim] bf16, post-base-RoPE
+ *   k    [batch, L, n_kv_heads, head_dim] bf16, post-base-RoPE
+ *   v    [batch, L, n_kv_heads, head_dim] bf16
+ *   o    [batch, L, n_q_heads,  head_dim] bf16, written
+ *   lse  [batch, n_q_heads, L] float32, written when not NULL
+ * Row i attends keys 0..i; G is computed once from the full L for every row.
+ * w0 >= L makes every pair local (plain causal RoPE attention); w0 = 0 makes every pair
+ * remote. head_dim must be 64 or 128; n_q_heads must be a multiple of n_kv_heads.
+ * Limits: L <= 2^30, batch * L * heads * head_dim < 2^62.
+ * Returns BIFOCAL_OK or a negative bifocal_status. */
+int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                    int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta,
+                    void* stream);
+
+/* Bytes of device workspace bifocal_decode needs for any L <= max_L with these shapes.
+ * Returns 0 for invalid arguments (which bifocal_decode would reject anyway). */
+size_t bifocal_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                      int64_t max_L);
+
+/* One single-token decode step against a base-position KV cache (split-K + LSE reduce).
+ *   q        [batch, n_q_heads, head_dim] bf16: the new token's query, post-base-RoPE at
+ *            position p = L - 1
+ *   k_cache  [batch, cache_capacity, n_kv_heads, head_dim] bf16, positions 0..L-1 valid
+ *            (the new token's key/value already appended at L - 1); read only
+ *   v_cache  same layout as k_cache
+ *   o        [batch, n_q_heads, head_dim] bf16, written
+ *   lse      [batch, n_q_heads] float32, written when not NULL
+ *   workspace: device buffer of at least bifocal_decode_workspace_bytes(..., L) bytes,
+ *            owned by the caller; its contents need no initialisation and are clobbered.
+ * G is recomputed from this step's L (review page, Method: G follows the current length),
+ * so a stream of calls crosses a change of G with no cache rewrite. Calls that share a
+ * workspace must be ordered (same stream). head_dim must be 64 or 128, and
+ * n_q_heads / n_kv_heads must be 1, 2 or 4.
+ * Returns BIFOCAL_OK or a negative bifocal_status. */
+int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                   int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                   int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
+                   double rope_theta, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Parity hook for the position arithmetic: writes G (from L and w_pretrained) to
+ * G_out[0] and f(x) = floor(x / G) to f_out[x] for x < L, using the same device code the
+ * attention kernels use (gist.science summary, Methodologie section 1).
+ *   f_out [L] int32 device buffer; G_out [1] int32 device buffer.  L <= 2^31 - 1. */
+int bifocal_positions(int64_t L, int64_t w_pretrained, int32_t* f_out, int32_t* G_out,
+                      void* stream);
+
+/* Static, NUL-terminated, host-memory description of a status code (never NULL). */
+const char* bifocal_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIFOCAL_H_ */

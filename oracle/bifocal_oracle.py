@@ -134,20 +134,24 @@ def bifocal_attention(q, k, v, *, w0: int, w_pretrained: int, theta: float,
     positions. Query head h reads KV head h // (Hq / Hkv).
     `rows` optionally restricts the computed query rows (sorted or not); keys are always
     0 .. i for row i, and G is always taken from the full length L.
+    Only the requested rows (and the keys they reach) are converted to float64.
     Returns (O [B, R, Hq, D] float64, LSE [B, Hq, R] float64, natural log), R = len(rows).
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
     B, L, Hq, Hkv, D = _check_shapes(q, k, v)
     if w0 < 0:
         raise ValueError("w0 must be >= 0")
     G = group_size(L, w_pretrained)
     rows = np.arange(L, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
-    if rows.size and (rows.min() < 0 or rows.max() >= L):
+    if rows.size == 0:
+        return np.zeros((B, 0, Hq, D)), np.zeros((B, Hq, 0))
+    if rows.min() < 0 or rows.max() >= L:
         raise ValueError("row out of range")
-    q_rem = _remote_vectors(q, L, G, theta)
-    k_rem = _remote_vectors(k, L, G, theta)
+    nk = int(rows.max()) + 1
+    omega = rope_frequencies(D, theta)
+    delta = correction_offsets(L, G).astype(np.float64)
+    kf = np.asarray(k[:, :nk], dtype=np.float64)
+    vf = np.asarray(v[:, :nk], dtype=np.float64)
+    k_rem = rotate_pairs(kf, (delta[:nk, None] * omega[None, :])[None, :, None, :])
     group = Hq // Hkv
     scale = 1.0 / math.sqrt(D)
     out = np.zeros((B, rows.size, Hq, D), dtype=np.float64)
@@ -159,16 +163,18 @@ def bifocal_attention(q, k, v, *, w0: int, w_pretrained: int, theta: float,
         rel = r[:, None] - j[None, :]  # i - j
         local = (rel >= 0) & (rel < w0)
         remote = rel >= w0
+        qb = np.asarray(q[:, r], dtype=np.float64)  # [B, R, Hq, D]
+        qb_rem = rotate_pairs(qb, (delta[r][:, None] * omega[None, :])[None, :, None, :])
         for b in range(B):
             for h in range(Hq):
                 kv = h // group
-                s_base = (q[b, r, h, :] @ k[b, :nkeys, kv, :].T) * scale
-                s_rem = (q_rem[b, r, h, :] @ k_rem[b, :nkeys, kv, :].T) * scale
+                s_base = (qb[b, :, h, :] @ kf[b, :nkeys, kv, :].T) * scale
+                s_rem = (qb_rem[b, :, h, :] @ k_rem[b, :nkeys, kv, :].T) * scale
                 s = np.where(local, s_base, np.where(remote, s_rem, -np.inf))
                 m = s.max(axis=1, keepdims=True)
                 p = np.exp(s - m)
                 l = p.sum(axis=1, keepdims=True)
-                out[b, start:start + r.size, h, :] = (p @ v[b, :nkeys, kv, :]) / l
+                out[b, start:start + r.size, h, :] = (p @ vf[b, :nkeys, kv, :]) / l
                 lse[b, h, start:start + r.size] = (m + np.log(l))[:, 0]
     return out, lse
 

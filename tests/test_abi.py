@@ -1,0 +1,134 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared entry point, and
+rejects invalid arguments on the host before any HIP call.
+
+Fake device pointers below are only ever passed together with an argument the host check
+rejects, so no kernel is launched and nothing is dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import group_size
+from zero_shot_rope_amd import bifocal as B
+from zero_shot_rope_amd import build as build_mod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bifocal.h")
+OK, EINVAL, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4
+FAKE = 0x1000  # never dereferenced: every call using it fails a host-side check first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build_mod.LIB):
+        build_mod.build()
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bifocal_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(B.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(B.library_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_group_size_matches_oracle(lib):
+    for L in list(range(1, 300)) + [32767, 32768, 32769, 65536, 98304, 98305, 131072, 1 << 30]:
+        for wp in (1, 7, 128, 32768):
+            assert B.bifocal_group_size(L, wp) == group_size(L, wp)
+
+
+def test_group_size_rejects_bad_arguments(lib):
+    for L, wp in [(0, 1), (-1, 5), (5, 0), (5, -2)]:
+        assert lib.bifocal_group_size(L, wp) == EINVAL
+
+
+def test_status_strings(lib):
+    seen = set()
+    for st in (OK, EINVAL, EUNSUP, EWS, EHIP):
+        s = B.bifocal_status_string(st)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 5
+    assert B.bifocal_status_string(12345) == "unknown status"
+
+
+def prefill_call(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, batch=1, hq=4, hkv=2, d=128, L=256, w0=32,
+                wp=64, theta=1e4)
+    args.update(kw)
+    return lib.bifocal_prefill(args["q"], args["k"], args["v"], args["o"], args["lse"], args["batch"],
+                               args["hq"], args["hkv"], args["d"], args["L"], args["w0"], args["wp"],
+                               args["theta"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), EINVAL), (dict(k=None), EINVAL), (dict(v=None), EINVAL), (dict(o=None), EINVAL),
+    (dict(batch=0), EINVAL), (dict(hq=0), EINVAL), (dict(hkv=0), EINVAL), (dict(d=0), EINVAL),
+    (dict(L=0), EINVAL), (dict(L=-5), EINVAL), (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL),
+    (dict(theta=0.0), EINVAL), (dict(theta=-1.0), EINVAL), (dict(theta=float("nan")), EINVAL),
+    (dict(theta=float("inf")), EINVAL), (dict(hq=6, hkv=4), EINVAL),
+    (dict(d=96), EUNSUP), (dict(d=256), EUNSUP), (dict(L=(1 << 30) + 1), EUNSUP),
+])
+def test_prefill_rejects_before_any_hip_call(lib, kw, expect):
+    assert prefill_call(lib, **kw) == expect
+
+
+def decode_call(lib, **kw):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, batch=1, hq=8, hkv=2, d=128, L=100, cap=128,
+                w0=16, wp=32, theta=1e4, ws=FAKE, wsb=1 << 40)
+    args.update(kw)
+    return lib.bifocal_decode(args["q"], args["kc"], args["vc"], args["o"], args["lse"], args["batch"], args["hq"],
+                              args["hkv"], args["d"], args["L"], args["cap"], args["w0"], args["wp"], args["theta"],
+                              args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), EINVAL), (dict(kc=None), EINVAL), (dict(vc=None), EINVAL), (dict(o=None), EINVAL),
+    (dict(L=0), EINVAL), (dict(L=129), EINVAL), (dict(w0=-3), EINVAL), (dict(wp=0), EINVAL),
+    (dict(theta=0.0), EINVAL), (dict(hq=7, hkv=2), EINVAL), (dict(batch=0), EINVAL),
+    (dict(d=80), EUNSUP), (dict(hq=16, hkv=2), EUNSUP), (dict(hq=6, hkv=2), EUNSUP),
+    (dict(ws=None), EWS), (dict(wsb=0), EWS), (dict(wsb=16), EWS),
+])
+def test_decode_rejects_before_any_hip_call(lib, kw, expect):
+    assert decode_call(lib, **kw) == expect
+
+
+def test_decode_workspace_query(lib):
+    assert lib.bifocal_decode_workspace_bytes(0, 8, 2, 128, 100) == 0
+    assert lib.bifocal_decode_workspace_bytes(1, 8, 3, 128, 100) == 0
+    prev = 0
+    for L in [1, 31, 32, 33, 1000, 4096, 98001, 98512, 131072]:
+        n = lib.bifocal_decode_workspace_bytes(1, 32, 8, 128, L)
+        assert n >= prev and n % (130 * 4 * 32) == 0
+        prev = n
+    # The exact requirement is accepted (the call still fails later only on the fake data).
+    need = lib.bifocal_decode_workspace_bytes(1, 8, 2, 128, 100)
+    assert decode_call(lib, wsb=need - 1) == EWS
+
+
+def test_positions_rejects_bad_arguments(lib):
+    p = ctypes.cast(ctypes.c_void_p(FAKE), ctypes.POINTER(ctypes.c_int32))
+    assert lib.bifocal_positions(10, 4, None, p, None) == EINVAL
+    assert lib.bifocal_positions(10, 4, p, None, None) == EINVAL
+    assert lib.bifocal_positions(0, 4, p, p, None) == EINVAL
+    assert lib.bifocal_positions(10, 0, p, p, None) == EINVAL
+    assert lib.bifocal_positions(1 << 31, 4, p, p, None) == EINVAL
+
+
+def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("BIFOCAL_LIBRARY", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        B.load_library()

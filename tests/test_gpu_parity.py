@@ -1,0 +1,273 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 CPU oracle.
+
+Gates (fixed for the whole file):
+  * position arithmetic (G and f) bit-exact;
+  * bf16 outputs: max-abs <= 2e-2 and relative L2 <= 5e-3 against the oracle computed on
+    the same bf16-rounded inputs; LSE (natural log) within 2e-2 absolute.
+Small cases compare every row; the full-size workloads compare a deterministic row sample
+(the oracle computes those rows one by one) and check every row for finiteness.
+Guard regions around every output catch writes outside the declared shapes.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import aliased_positions, bifocal_attention, bifocal_decode, group_size
+from zero_shot_rope_amd import bifocal as Z
+from zero_shot_rope_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+LSE_ABS = 2e-2
+GUARD = 4096  # elements of sentinel after each output
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def f64(bits):
+    return W.bf16_bits_to_float32(bits).astype(np.float64)
+
+
+def guarded(shape, dtype):
+    n = int(np.prod(shape))
+    buf = torch.full((n + GUARD,), -7.0, dtype=dtype, device="cuda")
+    return buf, buf[:n].view(*shape)
+
+
+def assert_guard(buf, n):
+    tail = buf[n:].float()
+    assert torch.all(tail == -7.0), "write outside the output shape"
+
+
+def compare(gpu, ref, what):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    err = gpu - ref
+    max_abs = float(np.max(np.abs(err))) if err.size else 0.0
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30))
+    say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    assert max_abs <= MAX_ABS, f"{what}: max_abs {max_abs}"
+    assert rel <= REL_L2, f"{what}: rel_l2 {rel}"
+
+
+def run_prefill(bits, w0, wp, theta, want_lse=True):
+    q, k, v = dev(bits["q"]), dev(bits["k"]), dev(bits["v"])
+    B, L, Hq, D = q.shape
+    obuf, o = guarded((B, L, Hq, D), torch.bfloat16)
+    lbuf, lse = guarded((B, Hq, L), torch.float32)
+    Z.prefill(q, k, v, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert_guard(obuf, o.numel())
+    assert_guard(lbuf, lse.numel())
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------------------
+# Position arithmetic
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("L,wp", [(1, 1), (1, 32768), (513, 128), (1000, 7), (8192, 32768),
+                                  (65536, 32768), (98304, 32768), (98305, 32768), (131072, 32768),
+                                  (131073, 32768), (300000, 1000)])
+def test_positions_bit_exact(L, wp):
+    say(f"positions L={L} wp={wp}")
+    f, G = Z.positions(L, wp)
+    assert G == group_size(L, wp)
+    assert np.array_equal(f.cpu().numpy().astype(np.int64), aliased_positions(L, G))
+
+
+# ---------------------------------------------------------------------------------------
+# Prefill: small cases, every row
+# ---------------------------------------------------------------------------------------
+SMALL_PREFILL = [
+    # (batch, L, Hq, Hkv, D, w_pretrained, w0, theta)
+    (1, 512, 1, 1, 64, 128, 32, 1e4),       # the tiny workload's shape (G = 4)
+    (1, 300, 4, 1, 128, 64, 50, 1e6),       # ragged L, G = 5, 4:1 GQA
+    (2, 200, 4, 2, 64, 50, 17, 1e4),        # batch 2, 2:1 GQA
+    (1, 777, 8, 2, 128, 256, 100, 1e6),     # ragged, G = 4, 4:1 GQA
+    (1, 400, 2, 2, 128, 100, 0, 1e4),       # w0 = 0: every pair remote
+    (1, 257, 4, 4, 64, 64, 1, 1e4),         # w0 = 1: only the diagonal local, no GQA
+    (1, 333, 4, 1, 128, 100, 10000, 1e6),   # w0 >= L: every pair local
+    (1, 1000, 4, 2, 128, 2048, 100, 1e6),   # G = 1
+    (1, 1, 4, 1, 128, 1, 0, 1e4),           # L = 1
+    (1, 65, 2, 1, 64, 16, 5, 1e4),          # one key past a tile
+    (1, 300, 8, 1, 128, 64, 40, 1e4),       # 8:1 GQA (two head units per KV head)
+    (1, 150, 3, 1, 64, 32, 20, 1e4),        # 3:1 GQA
+    (1, 1100, 32, 8, 128, 300, 64, 1e6),    # Qwen3-8B heads, several query tiles, G = 4
+]
+
+
+@pytest.mark.parametrize("case", SMALL_PREFILL, ids=[f"B{c[0]}L{c[1]}H{c[2]}-{c[3]}D{c[4]}wp{c[5]}w{c[6]}" for c in SMALL_PREFILL])
+def test_prefill_small(case):
+    B, L, Hq, Hkv, D, wp, w0, theta = case
+    say(f"prefill small {case}")
+    bits = W.random_case(1000 + L + Hq, B, L, Hq, Hkv, D)
+    o, lse = run_prefill(bits, w0, wp, theta)
+    ref_o, ref_lse = bifocal_attention(f64(bits["q"]), f64(bits["k"]), f64(bits["v"]), w0=w0, w_pretrained=wp, theta=theta)
+    compare(o, ref_o, "o")
+    assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
+
+
+def test_prefill_tiny_workload():
+    cfg = W.TINY
+    say(f"prefill {cfg.name}")
+    bits = W.prefill_inputs(cfg)
+    o, lse = run_prefill(bits, cfg.w0, cfg.w_pretrained, cfg.rope_theta)
+    ref_o, ref_lse = bifocal_attention(f64(bits["q"]), f64(bits["k"]), f64(bits["v"]), w0=cfg.w0,
+                                       w_pretrained=cfg.w_pretrained, theta=cfg.rope_theta)
+    compare(o, ref_o, "o")
+    assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
+
+
+def test_prefill_in_window_workload_equals_plain_causal():
+    """Qwen3-1.7B layer shape at L = 8192 <= 32768: G = 1, the base model exactly."""
+    cfg = W.QWEN3_1_7B_8K
+    say(f"prefill {cfg.name}")
+    bits = W.prefill_inputs(cfg)
+    o, lse = run_prefill(bits, cfg.w0, cfg.w_pretrained, cfg.rope_theta)
+    o_ctrl, lse_ctrl = run_prefill(bits, cfg.L, cfg.w_pretrained, cfg.rope_theta)
+    assert np.array_equal(o, o_ctrl) and np.array_equal(lse, lse_ctrl)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(0, 70), [2047, 2048, 2049, 4095, 4096], rng.integers(0, cfg.L, 60),
+                                     np.arange(cfg.L - 70, cfg.L)]))
+    ref_o, ref_lse = bifocal_attention(f64(bits["q"]), f64(bits["k"]), f64(bits["v"]), w0=cfg.w0,
+                                       w_pretrained=cfg.w_pretrained, theta=cfg.rope_theta, rows=rows)
+    compare(o[:, rows], ref_o, "o(sampled rows)")
+    assert np.max(np.abs(lse[:, :, rows] - ref_lse)) <= LSE_ABS
+
+
+def sample_rows(L, w0, G, seed, n_random=24):
+    """Deterministic rows: the start, around w0 and 2*w0, tile edges, G multiples, the end."""
+    rng = np.random.default_rng(seed)
+    picks = [0, 1, 2, 63, 64, 65, 127, 128, w0 - 1, w0, w0 + 1, 2 * w0 - 1, 2 * w0, 2 * w0 + 1,
+             L // 2 - 1, L // 2, L // 2 + 1, L - 65, L - 64, L - 63, L - 2, L - 1]
+    m = (L // 3) // G * G
+    picks += [m - 1, m, m + 1]
+    picks += list(rng.integers(0, L, n_random))
+    return np.unique(np.clip(np.array(picks), 0, L - 1))
+
+
+def full_size_prefill(cfg, seed):
+    say(f"prefill {cfg.name} (full size, sampled rows)")
+    bits = W.prefill_inputs(cfg)
+    o, lse = run_prefill(bits, cfg.w0, cfg.w_pretrained, cfg.rope_theta)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    G = group_size(cfg.L, cfg.w_pretrained)
+    rows = sample_rows(cfg.L, cfg.w0, G, seed)
+    ref_o, ref_lse = _oracle_rows(bits, cfg, rows)
+    compare(o[:, rows], ref_o, "o(sampled rows)")
+    assert np.max(np.abs(lse[:, :, rows] - ref_lse)) <= LSE_ABS
+
+
+def _oracle_rows(bits, cfg, rows):
+    # The oracle reads only the sampled query rows and the keys they reach.
+    qv = W.bf16_bits_to_float32(bits["q"])
+    kv = W.bf16_bits_to_float32(bits["k"])
+    vv = W.bf16_bits_to_float32(bits["v"])
+    return bifocal_attention(qv, kv, vv, w0=cfg.w0, w_pretrained=cfg.w_pretrained, theta=cfg.rope_theta,
+                             rows=rows, block=16)
+
+
+@pytest.mark.parametrize("w0", [1024, 2048, 4096])
+def test_prefill_qwen3_4b_64k(w0):
+    full_size_prefill(W.QWEN3_4B_64K[w0], seed=40 + w0)
+
+
+def test_prefill_qwen3_8b_128k():
+    full_size_prefill(W.QWEN3_8B_128K, seed=41)
+
+
+# ---------------------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------------------
+def run_decode(q_bits, k_bits, v_bits, L, w0, wp, theta, workspace=None):
+    q, kc, vc = dev(q_bits), dev(k_bits), dev(v_bits)
+    B, Hq, D = q.shape
+    obuf, o = guarded((B, Hq, D), torch.bfloat16)
+    lbuf, lse = guarded((B, Hq), torch.float32)
+    Z.decode(q, kc, vc, L=L, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse, workspace=workspace)
+    torch.cuda.synchronize()
+    assert_guard(obuf, o.numel())
+    assert_guard(lbuf, lse.numel())
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+SMALL_DECODE = [
+    # (batch, cap, Hq, Hkv, D, w_pretrained, w0, theta, Ls)
+    (1, 1100, 4, 1, 128, 256, 100, 1e6, [511, 512, 513, 768, 769, 1025]),   # G flips 2->3->4->5
+    (2, 300, 4, 2, 64, 64, 17, 1e4, [1, 2, 31, 32, 33, 64, 65, 299]),
+    (1, 500, 2, 2, 128, 100, 0, 1e4, [100, 101, 450]),                       # all remote
+    (1, 500, 2, 1, 128, 100, 1, 1e4, [200, 333]),                            # only the new token local
+    (1, 400, 8, 2, 64, 64, 10000, 1e6, [257, 400]),                          # all local
+    (1, 3000, 32, 8, 128, 1000, 128, 1e6, [2000, 2001, 2999, 3000]),         # Qwen3-8B heads
+]
+
+
+@pytest.mark.parametrize("case", SMALL_DECODE, ids=[f"B{c[0]}cap{c[1]}H{c[2]}-{c[3]}D{c[4]}w{c[6]}" for c in SMALL_DECODE])
+def test_decode_small(case):
+    B, cap, Hq, Hkv, D, wp, w0, theta, Ls = case
+    rng = np.random.default_rng(cap + Hq)
+    kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    for L in Ls:
+        say(f"decode small {case[:8]} L={L}")
+        qb = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+        o, lse = run_decode(qb, kb, vb, L, w0, wp, theta)
+        ref_o, ref_lse = bifocal_decode(f64(qb), f64(kb), f64(vb), L=L, w0=w0, w_pretrained=wp, theta=theta)
+        compare(o, ref_o, f"o L={L}")
+        assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
+
+
+def test_decode_qwen3_8b_across_group_flip():
+    cfg = W.QWEN3_8B_DECODE
+    say(f"decode {cfg.name} (full cache)")
+    bits = W.decode_inputs(cfg)
+    kc, vc = dev(bits["k_cache"]), dev(bits["v_cache"])
+    kf = W.bf16_bits_to_float32(bits["k_cache"])
+    vf = W.bf16_bits_to_float32(bits["v_cache"])
+    ws = torch.empty(Z.bifocal_decode_workspace_bytes(1, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.capacity),
+                     dtype=torch.uint8, device="cuda")
+    for t in [0, 1, 303, 304, 305, 511]:
+        L = cfg.L_first + t
+        say(f"  step {t}: L={L} G={group_size(L, cfg.w_pretrained)}")
+        q = dev(bits["q_steps"][t])
+        obuf, o = guarded((1, cfg.n_q_heads, cfg.head_dim), torch.bfloat16)
+        lse = torch.empty((1, cfg.n_q_heads), dtype=torch.float32, device="cuda")
+        Z.decode(q, kc, vc, L=L, w0=cfg.w0, w_pretrained=cfg.w_pretrained, rope_theta=cfg.rope_theta,
+                 workspace=ws, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert_guard(obuf, o.numel())
+        ref_o, ref_lse = bifocal_decode(W.bf16_bits_to_float32(bits["q_steps"][t]), kf, vf, L=L, w0=cfg.w0,
+                                        w_pretrained=cfg.w_pretrained, theta=cfg.rope_theta)
+        compare(o.float().cpu().numpy(), ref_o, f"o step {t}")
+        assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= LSE_ABS
+
+
+def test_decode_matches_prefill_last_row_on_gpu():
+    B, L, Hq, Hkv, D, wp, w0, theta = 1, 700, 8, 2, 128, 200, 60, 1e6
+    bits = W.random_case(77, B, L, Hq, Hkv, D)
+    o_pre, lse_pre = run_prefill(bits, w0, wp, theta)
+    o_dec, lse_dec = run_decode(bits["q"][:, L - 1], bits["k"], bits["v"], L, w0, wp, theta)
+    compare(o_dec, o_pre[:, L - 1], "decode vs prefill row")
+    assert np.max(np.abs(lse_dec - lse_pre[:, :, L - 1])) <= 1e-3
+
+
+def test_calls_are_deterministic():
+    bits = W.random_case(5, 1, 600, 4, 1, 128)
+    a, la = run_prefill(bits, 40, 128, 1e6)
+    b, lb = run_prefill(bits, 40, 128, 1e6)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    qd = bits["q"][:, 599]
+    d1, _ = run_decode(qd, bits["k"], bits["v"], 600, 40, 128, 1e6)
+    d2, _ = run_decode(qd, bits["k"], bits["v"], 600, 40, 128, 1e6)
+    assert np.array_equal(d1, d2)

@@ -21,8 +21,8 @@ MUTATIONS = [
     ("window boundary off by one", "        local = (rel >= 0) & (rel < w0)", "        local = (rel >= 0) & (rel <= w0)"),
     ("remote boundary off by one", "        remote = rel >= w0", "        remote = rel > w0"),
     ("floor instead of ceil in G", "return max(1, -(-L // w_pretrained))", "return max(1, L // w_pretrained)"),
-    ("dropped query correction", "q_rem = _remote_vectors(q, L, G, theta)\n    k_rem = _remote_vectors(k, L, G, theta)\n    group = Hq // Hkv\n    scale",
-     "q_rem = q\n    k_rem = _remote_vectors(k, L, G, theta)\n    group = Hq // Hkv\n    scale"),
+    ("dropped query correction", "qb_rem = rotate_pairs(qb, (delta[r][:, None] * omega[None, :])[None, :, None, :])",
+     "qb_rem = qb"),
     ("correction sign", "return x // int(G) - x", "return x - x // int(G)"),
     ("frequency exponent", "-2.0 * k / head_dim", "-1.0 * k / head_dim"),
     ("score scale", "scale = 1.0 / math.sqrt(D)\n    out = np.zeros((B, rows.size", "scale = 1.0 / D\n    out = np.zeros((B, rows.size"),
@@ -41,8 +41,10 @@ def _load_mutant(old, new):
 
 
 def _pins_pass(m) -> bool:
-    """True if the (possibly mutated) oracle passes a compact set of the pins."""
-    try:
+    """True if the (possibly mutated) oracle passes a compact set of the pins.
+
+    A mutant that raises is reported by the caller, not counted as caught."""
+    if True:
         # Golden G values (review page, Validation/Significance; atlas summary, Approach).
         if m.group_size(131072, 32768) != 4 or m.group_size(32769, 32768) != 2 or m.group_size(8, 32768) != 1:
             return False
@@ -58,8 +60,6 @@ def _pins_pass(m) -> bool:
         q, k, v = _rand(60, 1, 40, 4, 2, 16)
         o, _ = m.bifocal_attention(q, k, v, w0=8, w_pretrained=64, theta=1e4)
         return bool(np.allclose(o, sdpa_causal(q, k, v), atol=1e-9, rtol=0))
-    except Exception:
-        return False
 
 
 def test_unmutated_oracle_passes_compact_pins():

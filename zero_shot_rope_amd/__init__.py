@@ -1,0 +1,14 @@
+"""MI355X-native Dynamic Bifocal RoPE attention (prefill + single-token decode).
+
+The compute runs in the HIP library libbifocal.so (C ABI in include/bifocal.h); this
+package only marshals torch tensors (device memory, the current stream) into that ABI.
+There is no fallback: if the library is missing, every entry point raises.
+
+Submodules:
+  bifocal    -- the binding: bifocal_prefill, bifocal_decode, bifocal_positions, ...
+  workloads  -- seeded synthetic inputs (no attention arithmetic)
+  build      -- compiles the library in-tree with hipcc for gfx950
+"""
+from .bifocal import (BifocalError, bifocal_decode, bifocal_decode_workspace_bytes, bifocal_group_size,  # noqa: F401
+                      bifocal_positions, bifocal_prefill, bifocal_status_string, decode, library_path,
+                      load_library, positions, prefill)

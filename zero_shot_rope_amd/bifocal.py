@@ -1,0 +1,201 @@
+"""ctypes binding of the bifocal attention C ABI (include/bifocal.h).
+
+Argument marshalling only: tensors become device pointers and sizes, the current torch
+stream becomes the hipStream_t, a negative status becomes a BifocalError. Every step of
+the attention runs in the HIP kernels of libbifocal.so. The library is required: when it
+is missing the entry points raise instead of computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libbifocal.so"
+_lock = threading.Lock()
+_lib = None
+
+EXPORTED_SYMBOLS = (
+    "bifocal_group_size",
+    "bifocal_prefill",
+    "bifocal_decode_workspace_bytes",
+    "bifocal_decode",
+    "bifocal_positions",
+    "bifocal_status_string",
+)
+
+
+class BifocalError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {bifocal_status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return os.environ.get("BIFOCAL_LIBRARY", os.path.join(HERE, _LIB_NAME))
+
+
+def load_library():
+    """dlopen libbifocal.so (once) and declare the C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"HIP library {path} is not built; run `python -m zero_shot_rope_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(path)
+        c_i64, c_int, c_vp, c_dbl, c_sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_double, ctypes.c_size_t
+        fp = ctypes.POINTER(ctypes.c_float)
+        lib.bifocal_group_size.argtypes = [c_i64, c_i64]
+        lib.bifocal_group_size.restype = c_i64
+        lib.bifocal_prefill.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
+                                        c_i64, c_i64, c_i64, c_dbl, c_vp]
+        lib.bifocal_prefill.restype = c_int
+        lib.bifocal_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_i64]
+        lib.bifocal_decode_workspace_bytes.restype = c_sz
+        lib.bifocal_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
+                                       c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
+        lib.bifocal_decode.restype = c_int
+        lib.bifocal_positions.argtypes = [c_i64, c_i64, ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int32), c_vp]
+        lib.bifocal_positions.restype = c_int
+        lib.bifocal_status_string.argtypes = [c_int]
+        lib.bifocal_status_string.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+# ---------------------------------------------------------------------------------------
+# Raw entry points (same names and argument order as the C ABI; pointers may be ints)
+# ---------------------------------------------------------------------------------------
+def bifocal_status_string(status: int) -> str:
+    return load_library().bifocal_status_string(int(status)).decode()
+
+
+def bifocal_group_size(L: int, w_pretrained: int) -> int:
+    return int(load_library().bifocal_group_size(int(L), int(w_pretrained)))
+
+
+def bifocal_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, max_L: int) -> int:
+    return int(load_library().bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, int(max_L)))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _fptr(t):
+    p = _ptr(t)
+    return None if p is None else ctypes.cast(ctypes.c_void_p(p), ctypes.POINTER(ctypes.c_float))
+
+
+def _stream(stream, device=None) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def bifocal_prefill(q, k, v, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, w0, w_pretrained,
+                    rope_theta, stream=None) -> None:
+    lib = load_library()
+    st = lib.bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), batch, n_q_heads, n_kv_heads,
+                             head_dim, int(L), int(w0), int(w_pretrained), float(rope_theta), _stream(stream))
+    if st != 0:
+        raise BifocalError(st, "bifocal_prefill")
+
+
+def bifocal_decode(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, cache_capacity,
+                   w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream=None) -> None:
+    lib = load_library()
+    st = lib.bifocal_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _fptr(lse), batch, n_q_heads,
+                            n_kv_heads, head_dim, int(L), int(cache_capacity), int(w0), int(w_pretrained),
+                            float(rope_theta), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise BifocalError(st, "bifocal_decode")
+
+
+def bifocal_positions(L, w_pretrained, f_out, G_out, stream=None) -> None:
+    lib = load_library()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    fo = None if f_out is None else ctypes.cast(ctypes.c_void_p(_ptr(f_out)), i32p)
+    go = None if G_out is None else ctypes.cast(ctypes.c_void_p(_ptr(G_out)), i32p)
+    st = lib.bifocal_positions(int(L), int(w_pretrained), fo, go, _stream(stream))
+    if st != 0:
+        raise BifocalError(st, "bifocal_positions")
+
+
+# ---------------------------------------------------------------------------------------
+# Tensor conveniences: shapes from the tensors, outputs allocated when not given
+# ---------------------------------------------------------------------------------------
+def _check(t, name, ndim):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 CUDA/HIP tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_theta: float, out=None, lse=None,
+            want_lse: bool = False, stream=None):
+    """q [B, L, Hq, D], k/v [B, L, Hkv, D] (bf16, post-base-RoPE) -> o (and lse [B, Hq, L])."""
+    import torch
+
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, 4)
+    B, L, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != L or k.shape[3] != D:
+        raise ValueError("k/v shapes do not match q")
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    bifocal_prefill(q, k, v, out, lse, B, Hq, k.shape[2], D, L, w0, w_pretrained, rope_theta,
+                    _stream(stream, q.device))
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def decode(q, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, rope_theta: float, workspace=None,
+           out=None, lse=None, want_lse: bool = False, stream=None):
+    """q [B, Hq, D]; caches [B, Lcap, Hkv, D] (bf16) -> o [B, Hq, D] (and lse [B, Hq])."""
+    import torch
+
+    _check(q, "q", 3)
+    _check(k_cache, "k_cache", 4)
+    _check(v_cache, "v_cache", 4)
+    B, Hq, D = q.shape
+    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shapes do not match q")
+    need = bifocal_decode_workspace_bytes(B, Hq, Hkv, D, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    bifocal_decode(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained, rope_theta,
+                   workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def positions(L: int, w_pretrained: int, device="cuda", stream=None):
+    """Run the device position arithmetic: returns (f int32 [L], G int)."""
+    import torch
+
+    f = torch.empty(L, dtype=torch.int32, device=device)
+    g = torch.empty(1, dtype=torch.int32, device=device)
+    bifocal_positions(L, w_pretrained, f, g, _stream(stream, f.device))
+    return f, int(g.item())

@@ -1,0 +1,156 @@
+// api.cpp -- C ABI of the bifocal attention library (declared in include/bifocal.h).
+//
+// Host responsibilities: validate every argument before any HIP call, compute the group
+// size G = max(1, ceil(L / w_pretrained)) in int64 (review page, Method; gist.science
+// summary, Methodologie section 1), turn the RoPE frequencies theta^(-2k/D) into 0.32
+// fixed-point phase increments in double precision, size the grids, launch on the
+// caller's stream. No allocation, no host synchronisation, no state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/bifocal.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr long long kMaxL = 1LL << 30;
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+// W_k = round(2^32 * frac(omega_k / (2 pi))) mod 2^32, omega_k = theta^(-2k/D).
+// frac() first, so that a frequency above one turn per step keeps its fractional part.
+void phase_increments(int head_dim, double theta, uint32_t* W) {
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int k = 0; k < head_dim / 2; ++k) {
+    const double omega = pow(theta, -2.0 * k / head_dim);
+    double turns = omega / two_pi;
+    turns -= floor(turns);
+    double fixed = nearbyint(turns * 4294967296.0);
+    if (fixed >= 4294967296.0) fixed -= 4294967296.0;
+    W[k] = static_cast<uint32_t>(fixed);
+  }
+}
+
+float scale_log2_for(int head_dim) {
+  return static_cast<float>(1.4426950408889634073599246810019 / sqrt(static_cast<double>(head_dim)));
+}
+
+int map_hip(hipError_t e) { return e == hipSuccess ? BIFOCAL_OK : BIFOCAL_EHIP; }
+
+bool sane_theta(double t) { return t > 0.0 && isfinite(t); }
+
+}  // namespace
+
+extern "C" {
+
+int64_t bifocal_group_size(int64_t L, int64_t w_pretrained) {
+  if (L < 1 || w_pretrained < 1) return BIFOCAL_EINVAL;
+  const int64_t g = L / w_pretrained + (L % w_pretrained != 0 ? 1 : 0);
+  return g < 1 ? 1 : g;
+}
+
+const char* bifocal_status_string(int status) {
+  switch (status) {
+    case BIFOCAL_OK: return "ok";
+    case BIFOCAL_EINVAL: return "invalid argument";
+    case BIFOCAL_EUNSUPPORTED: return "unsupported configuration";
+    case BIFOCAL_EWORKSPACE: return "decode workspace missing or too small";
+    case BIFOCAL_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                    int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta, void* stream) {
+  if (!q || !k || !v || !o) return BIFOCAL_EINVAL;
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
+  if (L < 1 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
+  if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
+  if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
+  if (L > kMaxL) return BIFOCAL_EUNSUPPORTED;
+  const long double elems = (long double)batch * (long double)L * n_q_heads * head_dim;
+  if (elems >= 4.0e18L) return BIFOCAL_EUNSUPPORTED;
+
+  const int64_t G = bifocal_group_size(L, w_pretrained);
+  uint32_t W[64];
+  phase_increments(head_dim, rope_theta, W);
+  bifocal::PrefillLaunch p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.batch = batch;
+  p.n_q_heads = n_q_heads;
+  p.n_kv_heads = n_kv_heads;
+  p.head_dim = head_dim;
+  p.L = static_cast<int>(L);
+  // G == 1 makes the correction rotation the identity, so every pair scores as a local one:
+  // run the all-local path (the base model exactly, with no rotation work).
+  p.w0 = (G == 1 || w0 >= L) ? static_cast<int>(L) : static_cast<int>(w0);
+  p.G = static_cast<int>(G);
+  p.scale_log2 = scale_log2_for(head_dim);
+  p.W = W;
+  return map_hip(bifocal::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t bifocal_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                      int64_t max_L) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1 || max_L < 1) return 0;
+  if (max_L > kMaxL || n_q_heads % n_kv_heads != 0) return 0;
+  const bifocal::DecodeSplit s = bifocal::decode_split(max_L, batch, n_kv_heads);
+  return static_cast<size_t>(batch) * n_q_heads * s.max_splits * (head_dim + 2) * sizeof(float);
+}
+
+int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                   int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                   int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
+                   double rope_theta, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !o) return BIFOCAL_EINVAL;
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
+  if (L < 1 || cache_capacity < L || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta))
+    return BIFOCAL_EINVAL;
+  if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
+  if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
+  const int group = n_q_heads / n_kv_heads;
+  if (group != 1 && group != 2 && group != 4) return BIFOCAL_EUNSUPPORTED;
+  if (cache_capacity > kMaxL || batch > 65535) return BIFOCAL_EUNSUPPORTED;  // grid z limit
+  const size_t need = bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L);
+  if (!workspace || workspace_bytes < need) return BIFOCAL_EWORKSPACE;
+
+  const int64_t G = bifocal_group_size(L, w_pretrained);
+  uint32_t W[64];
+  phase_increments(head_dim, rope_theta, W);
+  const bifocal::DecodeSplit s = bifocal::decode_split(L, batch, n_kv_heads);
+  bifocal::DecodeLaunch p;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.o = o;
+  p.lse = lse;
+  p.workspace = static_cast<float*>(workspace);
+  p.batch = batch;
+  p.n_q_heads = n_q_heads;
+  p.n_kv_heads = n_kv_heads;
+  p.head_dim = head_dim;
+  p.L = static_cast<int>(L);
+  p.capacity = static_cast<int>(cache_capacity);
+  p.w0 = (G == 1 || w0 >= L) ? static_cast<int>(L) : static_cast<int>(w0);
+  p.G = static_cast<int>(G);
+  p.n_splits = s.n_splits;
+  p.chunk = s.chunk;
+  p.scale_log2 = scale_log2_for(head_dim);
+  p.W = W;
+  return map_hip(bifocal::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int bifocal_positions(int64_t L, int64_t w_pretrained, int32_t* f_out, int32_t* G_out, void* stream) {
+  if (!f_out || !G_out) return BIFOCAL_EINVAL;
+  if (L < 1 || w_pretrained < 1 || L > 0x7fffffffLL) return BIFOCAL_EINVAL;
+  const int64_t G = bifocal_group_size(L, w_pretrained);
+  return map_hip(bifocal::launch_positions(static_cast<int>(L), static_cast<int>(G), f_out, G_out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

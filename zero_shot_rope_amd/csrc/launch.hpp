@@ -1,0 +1,52 @@
+// launch.hpp -- internal host-side launch descriptors (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bifocal {
+
+// Arguments already validated by the C ABI layer; sizes fit in int.
+struct PrefillLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int batch, n_q_heads, n_kv_heads, head_dim;
+  int L;
+  int w0;  // clamped to [0, L]
+  int G;
+  float scale_log2;      // log2(e) / sqrt(head_dim)
+  const uint32_t* W;     // head_dim / 2 fixed-point phase increments (host memory)
+};
+
+struct DecodeLaunch {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  void* o;
+  float* lse;
+  float* workspace;
+  int batch, n_q_heads, n_kv_heads, head_dim;
+  int L, capacity;
+  int w0;  // clamped to [0, L]
+  int G;
+  int n_splits, chunk;
+  float scale_log2;
+  const uint32_t* W;
+};
+
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
+hipError_t launch_positions(int L, int G, int32_t* f_out, int32_t* G_out, hipStream_t stream);
+
+// Decode split sizing shared by the workspace query and the launch.
+struct DecodeSplit {
+  int n_splits;
+  int chunk;  // keys per split, a multiple of 32
+  int max_splits;  // upper bound on n_splits for every length <= L (workspace sizing)
+};
+DecodeSplit decode_split(long long L, int batch, int n_kv_heads);
+
+}  // namespace bifocal

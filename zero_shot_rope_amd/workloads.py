@@ -28,12 +28,17 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Inputs here are finite Gaussian draws, so NaN handling is not needed; a NaN input raises.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    if not np.all(np.isfinite(x)):
-        raise ValueError("bf16 rounding expects finite inputs")
-    bits = x.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    rounded = (bits + 0x7FFF + lsb) >> 16
-    return rounded.astype(np.uint16)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_in = x.reshape(-1).view(np.uint32)
+    flat_out = out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat_in.size, step):
+        bits = flat_in[s:s + step]
+        # Finite values stay below 0xFF800000, so the 32-bit sum cannot wrap.
+        if np.any((bits & 0x7F800000) == 0x7F800000):
+            raise ValueError("bf16 rounding expects finite inputs")
+        flat_out[s:s + step] = ((bits + (0x7FFF + ((bits >> 16) & 1))) >> 16).astype(np.uint16)
+    return out
 
 
 def bf16_bits_to_float32(bits: np.ndarray) -> np.ndarray:
