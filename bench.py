@@ -75,10 +75,15 @@ def main():
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         log(f"decode cache {tuple(kc.shape)} ready")
     sptr = stream.cuda_stream
+    pws_bytes = Z.bifocal_prefill_workspace_bytes(pcfg.batch, pcfg.n_kv_heads, pcfg.head_dim, pcfg.L)
+    pws = torch.empty(pws_bytes, dtype=torch.uint8, device=dev)
 
-    def prefill(w0):
+    def prefill(w0, fused=False):
+        # Default: keys rotated once into the workspace, then the attention kernel. fused=True:
+        # no workspace, the attention kernel rotates each key tile as it stages it.
+        ws, nb = (None, 0) if fused else (pws, pws_bytes)
         Z.bifocal_prefill(q, k, v, o, None, pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim, pcfg.L, w0,
-                          pcfg.w_pretrained, pcfg.rope_theta, sptr)
+                          pcfg.w_pretrained, pcfg.rope_theta, ws, nb, sptr)
 
     def decode_steps():
         for t in range(dcfg.steps):
@@ -155,6 +160,16 @@ def main():
     torch.cuda.synchronize()
     ctrl_ms = (cev[0].elapsed_time(cev[1]) + cev[1].elapsed_time(cev[2])) / 2.0
     ctrl_tflops = flops / (ctrl_ms * 1e-3) / 1e12
+    # The single-launch mode (key rotation per staged tile, no workspace).
+    fev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    prefill(pcfg.w0, fused=True)
+    fev[0].record(stream)
+    prefill(pcfg.w0, fused=True)
+    fev[1].record(stream)
+    prefill(pcfg.w0, fused=True)
+    fev[2].record(stream)
+    torch.cuda.synchronize()
+    fused_ms = (fev[0].elapsed_time(fev[1]) + fev[1].elapsed_time(fev[2])) / 2.0
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -184,7 +199,10 @@ def main():
         "prefill_ms": round(pre_avg, 3),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_kernel<128>", "flops_per_launch": flops},
+                     "kernel": "prefill_kernel<128, prerotated> (+ rotate_keys_kernel)", "flops_per_launch": flops},
+        "prefill_mode": "keys rotated once into a workspace, then the fused attention kernel",
+        "single_launch_mode": {"what": "no workspace: key rotation per staged tile inside the attention kernel",
+                               "ms": round(fused_ms, 3), "TFLOP/s": round(flops / (fused_ms * 1e-3) / 1e12, 2)},
         "matched_control": {"what": "same kernel, w0 >= L (plain causal RoPE attention)",
                             "ms": round(ctrl_ms, 3), "TFLOP/s": round(ctrl_tflops, 2),
                             "bifocal_over_control": round(ctrl_ms / pre_avg, 4)},

@@ -43,7 +43,7 @@ typedef enum {
   BIFOCAL_OK = 0,
   BIFOCAL_EINVAL = -1,       /* null pointer, non-positive size, bad w0/theta, head mismatch */
   BIFOCAL_EUNSUPPORTED = -2, /* valid arguments the kernels do not implement (head_dim, group) */
-  BIFOCAL_EWORKSPACE = -3,   /* decode workspace missing or smaller than required */
+  BIFOCAL_EWORKSPACE = -3,   /* workspace missing (decode) or smaller than required */
   BIFOCAL_EHIP = -4          /* a HIP runtime call or kernel launch failed */
 } bifocal_status;
 
@@ -52,21 +52,35 @@ typedef enum {
  * Returns G >= 1, or BIFOCAL_EINVAL (< 0) when L < 1 or w_pretrained < 1. */
 int64_t bifocal_group_size(int64_t L, int64_t w_pretrained);
 
-/* Fused bifocal prefill (one kernel launch).
+/* Bytes of the optional bifocal_prefill workspace for these shapes: room for the corrected
+ * keys K' = R(Delta) K~ (same size as k). Returns 0 for invalid arguments. */
+size_t bifocal_prefill_workspace_bytes(int batch, int n_kv_heads, int head_dim, int64_t L);
+
+/* Fused bifocal prefill: every pair routed by index, local/remote contributions merged by
+ * log-sum-exp in registers, one attention kernel launch.
  *   q    [batch, L, n_q_heads,  head_dim] bf16, post-base-RoPE
  *   k    [batch, L, n_kv_heads, head_dim] bf16, post-base-RoPE
  *   v    [batch, L, n_kv_heads, head_dim] bf16
  *   o    [batch, L, n_q_heads,  head_dim] bf16, written
  *   lse  [batch, n_q_heads, L] float32, written when not NULL
+ *   workspace / workspace_bytes: optional device buffer owned by the caller.
+ *     NULL: the attention kernel applies the key correction rotation to each key tile as it
+ *           stages it (single launch, no extra memory).
+ *     non-NULL (>= bifocal_prefill_workspace_bytes): a first small kernel writes the
+ *           corrected keys once into the workspace and the attention kernel reads them
+ *           (two launches; the rotation is done once per key instead of once per key tile
+ *           visit). Contents need no initialisation and are clobbered; calls sharing a
+ *           workspace must be ordered (same stream).
  * Row i attends keys 0..i; G is computed once from the full L for every row.
  * w0 >= L makes every pair local (plain causal RoPE attention); w0 = 0 makes every pair
  * remote. head_dim must be 64 or 128; n_q_heads must be a multiple of n_kv_heads.
  * Limits: L <= 2^30, batch * L * heads * head_dim < 2^62.
- * Returns BIFOCAL_OK or a negative bifocal_status. */
+ * Returns BIFOCAL_OK or a negative bifocal_status (BIFOCAL_EWORKSPACE when a non-NULL
+ * workspace is smaller than required). */
 int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                     int batch, int n_q_heads, int n_kv_heads, int head_dim,
                     int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta,
-                    void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace bifocal_decode needs for any L <= max_L with these shapes.
  * Returns 0 for invalid arguments (which bifocal_decode would reject anyway). */

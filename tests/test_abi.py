@@ -68,9 +68,11 @@ def prefill_call(lib, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, batch=1, hq=4, hkv=2, d=128, L=256, w0=32,
                 wp=64, theta=1e4)
     args.update(kw)
+    args.setdefault("ws", None)
+    args.setdefault("wsb", 0)
     return lib.bifocal_prefill(args["q"], args["k"], args["v"], args["o"], args["lse"], args["batch"],
                                args["hq"], args["hkv"], args["d"], args["L"], args["w0"], args["wp"],
-                               args["theta"], None)
+                               args["theta"], args["ws"], args["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -80,6 +82,7 @@ def prefill_call(lib, **kw):
     (dict(theta=0.0), EINVAL), (dict(theta=-1.0), EINVAL), (dict(theta=float("nan")), EINVAL),
     (dict(theta=float("inf")), EINVAL), (dict(hq=6, hkv=4), EINVAL),
     (dict(d=96), EUNSUP), (dict(d=256), EUNSUP), (dict(L=(1 << 30) + 1), EUNSUP),
+    (dict(ws=FAKE, wsb=0), EWS), (dict(ws=FAKE, wsb=256 * 2 * 128 * 2 - 1), EWS),
 ])
 def test_prefill_rejects_before_any_hip_call(lib, kw, expect):
     assert prefill_call(lib, **kw) == expect
@@ -132,3 +135,10 @@ def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         B.load_library()
+
+
+def test_prefill_workspace_query(lib):
+    assert lib.bifocal_prefill_workspace_bytes(1, 8, 128, 131072) == 131072 * 8 * 128 * 2
+    assert lib.bifocal_prefill_workspace_bytes(2, 2, 64, 100) == 2 * 100 * 2 * 64 * 2
+    for bad in [(0, 8, 128, 10), (1, 0, 128, 10), (1, 8, 96, 10), (1, 8, 128, 0), (1, 8, 128, (1 << 30) + 1)]:
+        assert lib.bifocal_prefill_workspace_bytes(*bad) == 0

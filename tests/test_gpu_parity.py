@@ -61,15 +61,24 @@ def compare(gpu, ref, what):
     assert rel <= REL_L2, f"{what}: rel_l2 {rel}"
 
 
-def run_prefill(bits, w0, wp, theta, want_lse=True):
+def run_prefill(bits, w0, wp, theta, mode="prerotated"):
+    """mode "fused": no workspace (keys rotated per tile in the attention kernel);
+    "prerotated": keys rotated once into a (guarded) workspace first."""
     q, k, v = dev(bits["q"]), dev(bits["k"]), dev(bits["v"])
     B, L, Hq, D = q.shape
     obuf, o = guarded((B, L, Hq, D), torch.bfloat16)
     lbuf, lse = guarded((B, Hq, L), torch.float32)
-    Z.prefill(q, k, v, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse)
+    ws = None
+    if mode == "prerotated":
+        nws = Z.bifocal_prefill_workspace_bytes(B, k.shape[2], D, L)
+        wbuf = torch.full((nws + GUARD,), 0x5A, dtype=torch.uint8, device="cuda")
+        ws = wbuf[:nws]
+    Z.prefill(q, k, v, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     assert_guard(obuf, o.numel())
     assert_guard(lbuf, lse.numel())
+    if ws is not None:
+        assert torch.all(wbuf[nws:] == 0x5A), "write outside the workspace"
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
 
@@ -107,12 +116,13 @@ SMALL_PREFILL = [
 ]
 
 
+@pytest.mark.parametrize("mode", ["prerotated", "fused"])
 @pytest.mark.parametrize("case", SMALL_PREFILL, ids=[f"B{c[0]}L{c[1]}H{c[2]}-{c[3]}D{c[4]}wp{c[5]}w{c[6]}" for c in SMALL_PREFILL])
-def test_prefill_small(case):
+def test_prefill_small(case, mode):
     B, L, Hq, Hkv, D, wp, w0, theta = case
-    say(f"prefill small {case}")
+    say(f"prefill small {case} {mode}")
     bits = W.random_case(1000 + L + Hq, B, L, Hq, Hkv, D)
-    o, lse = run_prefill(bits, w0, wp, theta)
+    o, lse = run_prefill(bits, w0, wp, theta, mode)
     ref_o, ref_lse = bifocal_attention(f64(bits["q"]), f64(bits["k"]), f64(bits["v"]), w0=w0, w_pretrained=wp, theta=theta)
     compare(o, ref_o, "o")
     assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
@@ -157,10 +167,10 @@ def sample_rows(L, w0, G, seed, n_random=24):
     return np.unique(np.clip(np.array(picks), 0, L - 1))
 
 
-def full_size_prefill(cfg, seed):
-    say(f"prefill {cfg.name} (full size, sampled rows)")
+def full_size_prefill(cfg, seed, mode="prerotated"):
+    say(f"prefill {cfg.name} (full size, sampled rows, {mode})")
     bits = W.prefill_inputs(cfg)
-    o, lse = run_prefill(bits, cfg.w0, cfg.w_pretrained, cfg.rope_theta)
+    o, lse = run_prefill(bits, cfg.w0, cfg.w_pretrained, cfg.rope_theta, mode)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     G = group_size(cfg.L, cfg.w_pretrained)
     rows = sample_rows(cfg.L, cfg.w0, G, seed)
@@ -183,8 +193,9 @@ def test_prefill_qwen3_4b_64k(w0):
     full_size_prefill(W.QWEN3_4B_64K[w0], seed=40 + w0)
 
 
-def test_prefill_qwen3_8b_128k():
-    full_size_prefill(W.QWEN3_8B_128K, seed=41)
+@pytest.mark.parametrize("mode", ["prerotated", "fused"])
+def test_prefill_qwen3_8b_128k(mode):
+    full_size_prefill(W.QWEN3_8B_128K, seed=41, mode=mode)
 
 
 # ---------------------------------------------------------------------------------------
@@ -267,6 +278,8 @@ def test_calls_are_deterministic():
     a, la = run_prefill(bits, 40, 128, 1e6)
     b, lb = run_prefill(bits, 40, 128, 1e6)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+    c, lc = run_prefill(bits, 40, 128, 1e6, "fused")
+    compare(c, a.astype(np.float64), "fused vs prerotated")
     qd = bits["q"][:, 599]
     d1, _ = run_decode(qd, bits["k"], bits["v"], 600, 40, 128, 1e6)
     d2, _ = run_decode(qd, bits["k"], bits["v"], 600, 40, 128, 1e6)

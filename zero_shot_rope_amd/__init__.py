@@ -10,5 +10,5 @@ Submodules:
   build      -- compiles the library in-tree with hipcc for gfx950
 """
 from .bifocal import (BifocalError, bifocal_decode, bifocal_decode_workspace_bytes, bifocal_group_size,  # noqa: F401
-                      bifocal_positions, bifocal_prefill, bifocal_status_string, decode, library_path,
+                      bifocal_positions, bifocal_prefill, bifocal_prefill_workspace_bytes, bifocal_status_string, decode, library_path,
                       load_library, positions, prefill)

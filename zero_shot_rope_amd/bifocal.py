@@ -19,6 +19,7 @@ _lib = None
 
 EXPORTED_SYMBOLS = (
     "bifocal_group_size",
+    "bifocal_prefill_workspace_bytes",
     "bifocal_prefill",
     "bifocal_decode_workspace_bytes",
     "bifocal_decode",
@@ -52,8 +53,10 @@ def load_library():
         fp = ctypes.POINTER(ctypes.c_float)
         lib.bifocal_group_size.argtypes = [c_i64, c_i64]
         lib.bifocal_group_size.restype = c_i64
+        lib.bifocal_prefill_workspace_bytes.argtypes = [c_int, c_int, c_int, c_i64]
+        lib.bifocal_prefill_workspace_bytes.restype = c_sz
         lib.bifocal_prefill.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
-                                        c_i64, c_i64, c_i64, c_dbl, c_vp]
+                                        c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
         lib.bifocal_prefill.restype = c_int
         lib.bifocal_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_i64]
         lib.bifocal_decode_workspace_bytes.restype = c_sz
@@ -78,6 +81,10 @@ def bifocal_status_string(status: int) -> str:
 
 def bifocal_group_size(L: int, w_pretrained: int) -> int:
     return int(load_library().bifocal_group_size(int(L), int(w_pretrained)))
+
+
+def bifocal_prefill_workspace_bytes(batch: int, n_kv_heads: int, head_dim: int, L: int) -> int:
+    return int(load_library().bifocal_prefill_workspace_bytes(batch, n_kv_heads, head_dim, int(L)))
 
 
 def bifocal_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, max_L: int) -> int:
@@ -108,10 +115,11 @@ def _stream(stream, device=None) -> Optional[int]:
 
 
 def bifocal_prefill(q, k, v, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, w0, w_pretrained,
-                    rope_theta, stream=None) -> None:
+                    rope_theta, workspace=None, workspace_bytes=0, stream=None) -> None:
     lib = load_library()
     st = lib.bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), batch, n_q_heads, n_kv_heads,
-                             head_dim, int(L), int(w0), int(w_pretrained), float(rope_theta), _stream(stream))
+                             head_dim, int(L), int(w0), int(w_pretrained), float(rope_theta), _ptr(workspace),
+                             int(workspace_bytes), _stream(stream))
     if st != 0:
         raise BifocalError(st, "bifocal_prefill")
 
@@ -149,8 +157,12 @@ def _check(t, name, ndim):
 
 
 def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_theta: float, out=None, lse=None,
-            want_lse: bool = False, stream=None):
-    """q [B, L, Hq, D], k/v [B, L, Hkv, D] (bf16, post-base-RoPE) -> o (and lse [B, Hq, L])."""
+            want_lse: bool = False, workspace=None, stream=None):
+    """q [B, L, Hq, D], k/v [B, L, Hkv, D] (bf16, post-base-RoPE) -> o (and lse [B, Hq, L]).
+
+    `workspace`: None runs the single-launch fused mode; a tensor (>= the workspace query)
+    runs the mode that rotates the keys once into it first; "auto" allocates one.
+    """
     import torch
 
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -162,7 +174,11 @@ def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_theta: float, out=None,
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
-    bifocal_prefill(q, k, v, out, lse, B, Hq, k.shape[2], D, L, w0, w_pretrained, rope_theta,
+    if isinstance(workspace, str) and workspace == "auto":
+        workspace = torch.empty(bifocal_prefill_workspace_bytes(B, k.shape[2], D, L), dtype=torch.uint8,
+                                device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    bifocal_prefill(q, k, v, out, lse, B, Hq, k.shape[2], D, L, w0, w_pretrained, rope_theta, workspace, ws_bytes,
                     _stream(stream, q.device))
     return (out, lse) if (want_lse or lse is not None) else out
 

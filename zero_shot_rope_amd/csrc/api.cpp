@@ -54,15 +54,23 @@ const char* bifocal_status_string(int status) {
     case BIFOCAL_OK: return "ok";
     case BIFOCAL_EINVAL: return "invalid argument";
     case BIFOCAL_EUNSUPPORTED: return "unsupported configuration";
-    case BIFOCAL_EWORKSPACE: return "decode workspace missing or too small";
+    case BIFOCAL_EWORKSPACE: return "workspace missing or too small";
     case BIFOCAL_EHIP: return "HIP runtime error";
     default: return "unknown status";
   }
 }
 
+size_t bifocal_prefill_workspace_bytes(int batch, int n_kv_heads, int head_dim, int64_t L) {
+  if (batch < 1 || n_kv_heads < 1 || !supported_head_dim(head_dim) || L < 1 || L > kMaxL) return 0;
+  const long double bytes = (long double)batch * (long double)L * n_kv_heads * head_dim * 2;
+  if (bytes >= 4.0e18L) return 0;
+  return bifocal::prefill_workspace_bytes(batch, L, n_kv_heads, head_dim);
+}
+
 int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                     int batch, int n_q_heads, int n_kv_heads, int head_dim,
-                    int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta, void* stream) {
+                    int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o) return BIFOCAL_EINVAL;
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
   if (L < 1 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
@@ -72,12 +80,16 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
   const long double elems = (long double)batch * (long double)L * n_q_heads * head_dim;
   if (elems >= 4.0e18L) return BIFOCAL_EUNSUPPORTED;
 
+  if (workspace != nullptr && workspace_bytes < bifocal_prefill_workspace_bytes(batch, n_kv_heads, head_dim, L))
+    return BIFOCAL_EWORKSPACE;
+
   const int64_t G = bifocal_group_size(L, w_pretrained);
   uint32_t W[64];
   phase_increments(head_dim, rope_theta, W);
   bifocal::PrefillLaunch p;
   p.q = q;
   p.k = k;
+  p.krot = workspace;
   p.v = v;
   p.o = o;
   p.lse = lse;

@@ -203,24 +203,57 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs<D> a)
   }
 }
 
-// One workgroup per (query head, batch); thread t owns output element d = t.
+// One workgroup of 256 threads per (query head, batch): block max of the split maxima, per-split
+// weights in LDS, then thread (part, d) accumulates splits part, part+P, ... for element d.
+constexpr int kMaxSplits = 4096;
+
+__device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float y = __shfl_xor(x, off);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  __syncthreads();
+  return r;
+}
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
-                                                          float* __restrict__ lse, int Hq, int n_splits) {
+__global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
+                                                            float* __restrict__ lse, int Hq, int n_splits) {
+  constexpr int P = 256 / D;
+  __shared__ float s_wt[kMaxSplits];
+  __shared__ float s_red[4];
+  __shared__ float s_acc[256];
   const int head = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const float* src = ws + ((size_t)b * Hq + head) * n_splits * (D + 2);
-  float M = kNegBig;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, src[(size_t)s * (D + 2)]);
-  float acc = 0.f, den = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float* ps = src + (size_t)s * (D + 2);
-    const float w = fast_exp2(ps[0] - M);
-    den += w * ps[1];
-    acc += w * ps[2 + t];
+  float m = kNegBig;
+  for (int s = t; s < n_splits; s += 256) m = fmaxf(m, src[(size_t)s * (D + 2)]);
+  const float M = block_reduce(m, s_red, true);
+  float den = 0.f;
+  for (int s = t; s < n_splits; s += 256) {
+    const float w = fast_exp2(src[(size_t)s * (D + 2)] - M);
+    s_wt[s] = w;
+    den += w * src[(size_t)s * (D + 2) + 1];
   }
-  const float val = acc / den;
-  o[((size_t)b * Hq + head) * D + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
-  if (lse != nullptr && t == 0) lse[(size_t)b * Hq + head] = (M + __log2f(den)) * 0.69314718055994531f;
+  den = block_reduce(den, s_red, false);  // ends with a barrier: s_wt is complete
+  const int d = t % D, part = t / D;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int s = part; s < n_splits; s += P) acc += s_wt[s] * src[(size_t)s * (D + 2) + 2 + d];
+  s_acc[t] = acc;
+  __syncthreads();
+  if (t < D) {
+    float tot = 0.f;
+#pragma unroll
+    for (int q = 0; q < P; ++q) tot += s_acc[q * D + t];
+    o[((size_t)b * Hq + head) * D + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(tot / den));
+    if (lse != nullptr && t == 0) lse[(size_t)b * Hq + head] = (M + __log2f(den)) * 0.69314718055994531f;
+  }
 }
 
 DecodeSplit decode_split(long long L, int batch, int n_kv_heads) {
@@ -256,7 +289,7 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
   hipLaunchKernelGGL(decode_split_kernel<D>, dim3(p.n_splits, p.n_kv_heads, p.batch), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, p.batch), dim3(D), 0, stream,
+  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, p.batch), dim3(256), 0, stream,
                      (const float*)p.workspace, static_cast<uint16_t*>(p.o), p.lse, p.n_q_heads, p.n_splits);
   return hipGetLastError();
 }

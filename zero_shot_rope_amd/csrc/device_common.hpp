@@ -80,6 +80,41 @@ __device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, int delta, const u
   hi = ohi;
 }
 
+// Same rotation, with the results multiplied by `scale` before rounding to bf16.
+__device__ __forceinline__ void rotate8_scaled(u32x4& lo, u32x4& hi, int delta, const uint32_t* W, float scale) {
+  u32x4 olo, ohi;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float x0 = bf16lo(lo[w]), x1 = bf16hi(lo[w]);
+    float y0 = bf16lo(hi[w]), y1 = bf16hi(hi[w]);
+    float s0, c0, s1, c1;
+    turns_sincos(phase_turns(delta, W[2 * w]), s0, c0);
+    turns_sincos(phase_turns(delta, W[2 * w + 1]), s1, c1);
+    olo[w] = pack_bf16x2((x0 * c0 - y0 * s0) * scale, (x1 * c1 - y1 * s1) * scale);
+    ohi[w] = pack_bf16x2((x0 * s0 + y0 * c0) * scale, (x1 * s1 + y1 * c1) * scale);
+  }
+  lo = olo;
+  hi = ohi;
+}
+
+// Eight bf16 values times `scale`, rounded back to bf16.
+__device__ __forceinline__ u32x4 scale8(u32x4 x, float scale) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) r[w] = pack_bf16x2(bf16lo(x[w]) * scale, bf16hi(x[w]) * scale);
+  return r;
+}
+
+// acc + lo(pk) + hi(pk) for a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t pk, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+}
+
+// True on every lane when `pred` holds on any active lane of the wave.
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
 // ---------------------------------------------------------------------------------------
 // MFMA 32x32x16 bf16 -> f32. Operand/result lane layout (wave64):
 //   A[i][k]: lane i + 32*(k/8), element k%8      (k < 16)

@@ -10,6 +10,7 @@ namespace bifocal {
 struct PrefillLaunch {
   const void* q;
   const void* k;
+  void* krot;  // NULL: fused in-kernel key rotation; else workspace for K' (prerotated mode)
   const void* v;
   void* o;
   float* lse;
@@ -39,6 +40,7 @@ struct DecodeLaunch {
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
+size_t prefill_workspace_bytes(long long batch, long long L, int n_kv_heads, int head_dim);
 hipError_t launch_positions(int L, int G, int32_t* f_out, int32_t* G_out, hipStream_t stream);
 
 // Decode split sizing shared by the workspace query and the launch.

@@ -1,32 +1,39 @@
 // prefill.hip -- fused Dynamic Bifocal RoPE prefill attention for gfx950 (MI355X).
 //
-// One launch computes, for every query row i and query head, softmax attention over keys
-// 0..i in which a pair is LOCAL when 0 <= i-j < w0 (base RoPE score q~_i . k~_j) and REMOTE
-// when i-j >= w0 (score of the vectors moved to the aliased positions f(i), f(j), obtained
-// by the correction rotation Delta = f(x) - x of the post-RoPE q~, k~).
+// One attention launch computes, for every query row i and query head, softmax attention over
+// keys 0..i in which a pair is LOCAL when 0 <= i-j < w0 (base RoPE score q~_i . k~_j) and
+// REMOTE when i-j >= w0 (score of the vectors moved to the aliased positions f(i), f(j) by the
+// correction rotation Delta = f(x) - x of the post-RoPE q~, k~).
 // Sources: review page "Paper Review -- Jet-Long", section Method (routing, the three
 // attentions and their inclusion-exclusion merge, fusion into one kernel); gist.science
 // summary, Methodologie section 2 (correction rotation by additive composition; the merge
 // reaches the exact routing output with no mask matrix, stabilised by log-sum-exp).
 //
-// The inclusion-exclusion merge (W_A O_A + W_B O_B - W_C O_C) / (W_A + W_B - W_C) is
-// realised in registers: B minus C is exactly the set of remote pairs, so the kernel
-// routes each score by its index (no mask matrix) and accumulates local and remote
-// contributions with a shared running max into one numerator, keeping separate per-row
-// sums for the local (A) and remote (B - C) weights; the epilogue merges them by LSE.
-// Nothing is ever subtracted, so there is no cancellation when W_C is close to W_B.
+// Inclusion-exclusion in registers: pass B minus pass C is exactly the set of remote pairs,
+// so the kernel routes each score by its index (no mask matrix) and accumulates local and
+// remote contributions against one running max into one numerator, keeping the local (A)
+// and remote (B - C) weights as separate per-row sums; the epilogue merges them by LSE.
+// Nothing is subtracted, so there is no cancellation when W_C is close to W_B.
+//
+// Key correction rotation K' = R(Delta_j) K~, two modes:
+//   fused       -- rotated per key tile while the tile is staged into LDS (no workspace);
+//   prerotated  -- rotate_keys_kernel writes K' once per call into a caller workspace and the
+//                  attention kernel stages K' tiles directly. Rotation is O(L*D) work; fused
+//                  repeats it for every query tile that visits a key tile (L/BM times) inside a
+//                  VALU-bound loop, so the prerotated mode is the fast one on CDNA4.
 //
 // Work decomposition
-//   workgroup = 256 threads = 4 waves; one KV head, BM query positions, hpw query heads
-//   (hpw = 4 for the 4:1 GQA of Qwen3-4B/8B, so all four heads share each staged K/V tile)
-//   wave      = one query head x 64 query rows (two 32-column MFMA blocks)
-//   key tile  = 64 keys: K~ (band tiles) and/or K' = R(Delta_j) K~ (tiles with remote pairs)
-//               and V^T staged in LDS; the K' rotation is done once per tile per workgroup
-//               while staging, shared by the 4 heads.
-//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16, so each lane owns one query column: the row max
-//   and sum are in-lane plus one v_permlane32_swap; P^T feeds the PV MFMA straight from the
-//   S^T registers; O^T = V^T P^T accumulates in 128 VGPRs per lane.
-//   Workgroup ids are remapped so that the 8 XCDs each take a contiguous range of
+//   workgroup = 256 threads = 4 waves (one per SIMD); one KV head, BM query positions, hpw
+//   query heads (hpw = 4 for the 4:1 GQA of Qwen3-4B/8B, so all four heads share each staged
+//   K/V tile). wave = one query head x 64 query rows (two 32-column MFMA blocks).
+//   key tile = 64 keys; K' (tiles with remote pairs), K~ (tiles with local pairs) and V^T are
+//   double-buffered in LDS; tile kt+1 is fetched into registers while tile kt is computed.
+//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query column, so the row max
+//   and sum are in-lane plus one v_permlane32_swap; P^T feeds the PV MFMA from registers;
+//   O^T = V^T P^T accumulates in 128 registers per lane. Q is pre-scaled by log2(e)/sqrt(D),
+//   so scores arrive in log2 units. The running max is only raised when a tile's max exceeds
+//   it by more than kSlack (the output is rescaled then); otherwise exponents stay <= kSlack.
+//   Workgroup ids are remapped so that each of the 8 XCDs owns a contiguous range of
 //   (batch, head unit, query tile) work, longest causal rows first.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -37,6 +44,7 @@ template <int D>
 struct PrefillArgs {
   const uint16_t* q;
   const uint16_t* k;
+  const uint16_t* krot;  // prerotated mode: K' = R(Delta) K~, same layout as k
   const uint16_t* v;
   uint16_t* o;
   float* lse;
@@ -50,23 +58,71 @@ struct PrefillArgs {
   uint32_t W[D / 2];
 };
 
-constexpr int kBN = 64;  // keys per tile
+constexpr int kBN = 64;         // keys per tile
+constexpr float kSlack = 8.0f;  // log2 units a row max may run ahead of the stored max
 
 template <int D>
+struct Tile {
+  static constexpr int HALF = D / 2;
+  static constexpr int NC = D / 16;        // MFMA k-steps over d
+  static constexpr int NDB = D / 32;       // 32-row d blocks of O^T
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;     // rows per wave-wide 1 KB direct load
+  static constexpr int NLD = kBN / RPI / 4;  // direct loads per wave per tile (4 waves)
+  static constexpr int MCH = HALF / 8;     // 8-pair chunks per half row
+  static constexpr int KREP = kBN * MCH / 256;  // fused-mode K staging units per thread
+  static constexpr int TSZ = kBN * D;      // elements per tile (rows are unpadded)
+};
+
+// Key/value tiles are stored row-major with 16-byte chunk `c` of row `r` at position
+// c ^ swz(r). swz permutes 0..7 so that (a) 8 consecutive rows read at one chunk (the K
+// operand, ds_read_b128) hit 8 distinct bank groups and (b) 4 consecutive rows read at a
+// chunk pair (the transposed V operand, ds_read_b64_tr_b16) hit 4 distinct pairs.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Fused mode: registers holding the key rows a thread rotates on their way to LDS.
+template <int D>
+struct Staged {
+  u32x4 rlo[Tile<D>::KREP], rhi[Tile<D>::KREP];  // key halves (d < D/2, d >= D/2)
+};
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void load_lds16(const void* g, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposed read: within each 16-lane group, lane r names 4 consecutive bf16 of row r of a
+// 16x4 block M; lane i receives M[4e + i/4][i%4] for e = 0..3.
+__device__ __forceinline__ u32x2 read_tr(const uint16_t* lds) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(lds));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
+
+// Kernel variants: every pair local (plain causal RoPE attention: w0 >= L or G = 1), or
+// bifocal with the key rotation done while staging (fused) or read from a workspace.
+enum PrefillMode { kLocalOnly = 0, kFused = 1, kPrerotated = 2 };
+
+// Two passes over the key tiles of a query tile, sharing one running max and one numerator:
+//   pass A (local):  tiles holding pairs with 0 <= i-j < w0, base scores q~ . k~, weight W_A;
+//   pass R (remote): tiles holding pairs with i-j >= w0, aliased scores q' . k', weight W_B - W_C.
+// Each pair is scored in exactly one pass (the other pass masks it by index), so the sum of the
+// two passes is the inclusion-exclusion merge with no subtraction. Pass A runs first, from the
+// diagonal down; only one of q~ / q' is held in registers at a time.
+template <int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(const PrefillArgs<D> a) {
-  constexpr int HALF = D / 2;
-  constexpr int NC = D / 16;   // MFMA k-steps over d
-  constexpr int NDB = D / 32;  // 32-row d blocks of O^T
-  constexpr int KP = D + 8;    // K tile pitch (bf16): row stride = 4 banks mod 32
-  constexpr int VP = kBN + 4;  // V^T tile pitch (bf16): row stride = 2 banks mod 32
-  constexpr int MCH = HALF / 8;             // 8-pair chunks per half row
-  constexpr int KUNITS = kBN * MCH;         // (key, chunk) staging units per tile
-  constexpr int VUNITS = (kBN / 4) * (D / 8);  // (4 keys x 8 d) transpose units per tile
+  using T = Tile<D>;
+  constexpr int HALF = T::HALF, NC = T::NC, NDB = T::NDB, CPR = T::CPR, RPI = T::RPI, MCH = T::MCH;
+  constexpr bool kBif = MODE != kLocalOnly;
 
-  __shared__ __align__(16) uint16_t s_krem[kBN * KP];
-  __shared__ __align__(16) uint16_t s_kloc[kBN * KP];
-  __shared__ __align__(16) uint16_t s_vt[D * VP];
+  __shared__ __align__(16) uint16_t s_k[2][T::TSZ];
+  __shared__ __align__(16) uint16_t s_v[2][T::TSZ];
   __shared__ uint32_t s_w[HALF];
 
   const int tid = threadIdx.x;
@@ -81,240 +137,279 @@ void prefill_kernel(const PrefillArgs<D> a) {
   const int bu = work / a.n_tiles;
   const int unit = bu % a.n_units, b = bu / a.n_units;
   const int Hg = a.Hq / a.Hkv;
-  const int upk = Hg / a.hpw;  // head units per KV head
+  const int upk = Hg / a.hpw;
   const int kvh = unit / upk;
   const int head = kvh * Hg + (unit % upk) * a.hpw + (wave % a.hpw);
   const int BM = 64 * (4 / a.hpw);
   const int i0 = tile * BM;
   const int iw = i0 + (wave / a.hpw) * 64;
   const int L = a.L, w0 = a.w0, G = a.G;
+  const float qscale = a.scale_log2;
 
   for (int t = tid; t < HALF; t += 256) s_w[t] = a.W[t];
   __syncthreads();
 
-  // ---- query operands (B of S^T = K Q^T): lane (col, h) holds q[i][16c + 8h .. +8] ----
-  u32x4 qt[2][NC], qr[2][NC];
   const size_t q_row_stride = (size_t)a.Hq * D;
+  // Query operand (B of S^T = K Q^T): lane (col, h) of row block qb holds q[i][16c + 8h .. +8],
+  // scaled into log2 units; with `rotate` the correction rotation R(Delta_i) is applied first.
+  auto load_q = [&](bool rotate, u32x4 (&dst)[2][NC]) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int i = iw + 32 * qb + col;
-    const uint16_t* src = a.q + ((size_t)b * L + i) * q_row_stride + (size_t)head * D + 8 * h;
+    for (int qb = 0; qb < 2; ++qb) {
+      const int i = iw + 32 * qb + col;
+      const uint16_t* src = a.q + ((size_t)b * L + i) * q_row_stride + (size_t)head * D + 8 * h;
+      u32x4 raw[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qt[qb][c] = u32x4{0, 0, 0, 0};
-      if (i < L) qt[qb][c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+      for (int c = 0; c < NC; ++c) {
+        raw[c] = u32x4{0, 0, 0, 0};
+        if (i < L) raw[c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+      }
+      if (rotate) {
+        const int dq = correction_offset(i < L ? i : 0, G);
+#pragma unroll
+        for (int c = 0; c < NC / 2; ++c) {
+          u32x4 lo = raw[c], hi = raw[c + NC / 2];
+          rotate8_scaled(lo, hi, dq, &s_w[16 * c + 8 * h], qscale);
+          dst[qb][c] = lo;
+          dst[qb][c + NC / 2] = hi;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) dst[qb][c] = scale8(raw[c], qscale);
+      }
     }
-    const int dq = correction_offset(i < L ? i : 0, G);
-#pragma unroll
-    for (int c = 0; c < NC / 2; ++c) {
-      u32x4 lo = qt[qb][c], hi = qt[qb][c + NC / 2];
-      rotate8(lo, hi, dq, &s_w[16 * c + 8 * h]);
-      qr[qb][c] = lo;
-      qr[qb][c + NC / 2] = hi;
-    }
-  }
+  };
 
-  // ---- per-thread staging constants ----
-  const int m_chunk = tid % MCH;  // fixed because 256 is a multiple of MCH
-  uint32_t wk[8];
+  const int i_last = min(i0 + BM, L) - 1;
+  const int iw_last = min(iw + 63, L - 1);
+  const bool wave_live = iw <= L - 1;
+  const size_t kv_row_stride = (size_t)a.Hkv * D;
+  const size_t kv_off = (size_t)b * L * kv_row_stride + (size_t)kvh * D;
+  const uint16_t* kbase = a.k + kv_off;
+  const uint16_t* vbase = a.v + kv_off;
+
+  // ---- staging ----
+  // Direct loads: wave w fills rows RPI*(NLD*w + n) + lane/CPR, lane slot lane%CPR, which holds
+  // global chunk (slot ^ swz(row)) of that row. Rows past L are clamped to L-1: their scores
+  // are masked (j > i) and their weights are 0.
+  const int ld_row0 = RPI * T::NLD * wave + lane / CPR;
+  const int ld_slot = lane % CPR;
+  auto stage_direct = [&](const uint16_t* src, uint16_t* tile, int j0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) wk[e] = s_w[8 * m_chunk + e];
+    for (int n = 0; n < T::NLD; ++n) {
+      const int row = ld_row0 + RPI * n;
+      const int j = min(j0 + row, L - 1);
+      const int chunk = ld_slot ^ swz(row);
+      load_lds16(src + (size_t)j * kv_row_stride + 8 * chunk, tile + (RPI * T::NLD * wave + RPI * n) * D);
+    }
+  };
+  // Fused mode: thread -> (key, 8-pair chunk) units, rotated in registers, written swizzled.
+  const int m_chunk = tid % MCH;
+  auto fetch_k = [&](int kt, Staged<D>& st) __attribute__((always_inline)) {
+    const int j0 = kt * kBN;
+#pragma unroll
+    for (int rep = 0; rep < T::KREP; ++rep) {
+      const int j = min(j0 + (tid + 256 * rep) / MCH, L - 1);
+      const uint16_t* src = kbase + (size_t)j * kv_row_stride + 8 * m_chunk;
+      st.rlo[rep] = *reinterpret_cast<const u32x4*>(src);
+      st.rhi[rep] = *reinterpret_cast<const u32x4*>(src + HALF);
+    }
+  };
+  auto commit_k = [&](int kt, uint16_t* tile, Staged<D>& st) __attribute__((always_inline)) {
+    const int j0 = kt * kBN;
+#pragma unroll
+    for (int rep = 0; rep < T::KREP; ++rep) {
+      const int key = (tid + 256 * rep) / MCH;
+      u32x4 lo = st.rlo[rep], hi = st.rhi[rep];
+      rotate8(lo, hi, correction_offset(j0 + key, G), &s_w[8 * m_chunk]);
+      uint16_t* row = tile + key * D;
+      *reinterpret_cast<u32x4*>(row + 8 * (m_chunk ^ swz(key))) = lo;
+      *reinterpret_cast<u32x4*>(row + 8 * ((m_chunk + MCH) ^ swz(key))) = hi;
+    }
+  };
 
   f32x16 o[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db][0] = o[db][1] = f32x16{};
   float m_run[2] = {kNegBig, kNegBig};
-  float l_loc[2] = {0.f, 0.f}, l_rem[2] = {0.f, 0.f};
+  float l_pass[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [pass: 0 local, 1 remote][qb]
 
-  const int i_last = min(i0 + BM, L) - 1;
-  const int n_kt = i_last / kBN + 1;
-  const int iw_last = min(iw + 63, L - 1);
-  const bool wave_live = iw <= L - 1;
-  const size_t kv_row_stride = (size_t)a.Hkv * D;
-  const uint16_t* kbase = a.k + (size_t)b * L * kv_row_stride + (size_t)kvh * D;
-  const uint16_t* vbase = a.v + (size_t)b * L * kv_row_stride + (size_t)kvh * D;
+  // LDS offsets of this lane's operands inside a tile.
+  // K (A of S^T): row 32kb + col, chunk 2c + h.  V (A of O^T via the transposed read): group
+  // g = lane/16 covers d = 32db + 16(g%2) + 0..15 and keys 16ch + 4h + 0..3 (+8 for elements 4..7).
+  const int tr_r = lane & 15;
+  const int tr_key = 4 * h + (tr_r >> 2);
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_r & 3);
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int j0 = kt * kBN;
-    // Workgroup-level classification decides what to stage.
-    const int g_max = i_last - j0, g_min = i0 - (j0 + kBN - 1);
-    const bool need_loc = (w0 > 0) && (g_max >= 0) && (g_min < w0);
-    const bool need_rem = g_max >= w0;
-
-    // ---- stage K~ / K' rows (row-major) ----
+  // One tile: S^T = K Q^T, optional index mask, online softmax (log2 units), O^T += V^T P^T.
+  // Kept pairs satisfy lo_rel <= i - j (and i - j < w0 in the local pass).
+  auto tile_step = [&](int buf, const u32x4 (&qa)[2][NC], int j0, bool masked, int lo_rel,
+                       bool local_pass) __attribute__((always_inline)) {
+    const int pass = local_pass ? 0 : 1;
+    f32x16 s[2][2];
+    const uint16_t* ks = s_k[buf];
 #pragma unroll
-    for (int rep = 0; rep < KUNITS / 256; ++rep) {
-      const int u = tid + 256 * rep;
-      const int key = u / MCH;
-      const int j = j0 + key;
-      u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-      if (j < L) {
-        const uint16_t* src = kbase + (size_t)j * kv_row_stride + 8 * m_chunk;
-        lo = *reinterpret_cast<const u32x4*>(src);
-        hi = *reinterpret_cast<const u32x4*>(src + HALF);
-      }
-      uint16_t* row_l = s_kloc + key * KP + 8 * m_chunk;
-      uint16_t* row_r = s_krem + key * KP + 8 * m_chunk;
-      if (need_loc) {
-        *reinterpret_cast<u32x4*>(row_l) = lo;
-        *reinterpret_cast<u32x4*>(row_l + HALF) = hi;
-      }
-      if (need_rem) {
-        rotate8(lo, hi, correction_offset(j, G), wk);
-        *reinterpret_cast<u32x4*>(row_r) = lo;
-        *reinterpret_cast<u32x4*>(row_r + HALF) = hi;
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb][0] = s[kb][1] = f32x16{};
+      const int row = 32 * kb + col;
+      const uint16_t* krow = ks + row * D;
+      const int sw = swz(row);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * c + h) ^ sw));
+        s[kb][0] = mfma32(av, qa[0][c], s[kb][0]);
+        s[kb][1] = mfma32(av, qa[1][c], s[kb][1]);
       }
     }
-    // ---- stage V^T: each unit transposes 4 keys x 8 d in registers ----
-    if (tid < VUNITS) {
-      const int kg = tid / (D / 8), dg = tid % (D / 8);
-      u32x4 row[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * kg + r;
-        row[r] = u32x4{0, 0, 0, 0};
-        if (j < L) row[r] = *reinterpret_cast<const u32x4*>(vbase + (size_t)j * kv_row_stride + 8 * dg);
-      }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1;
-        u32x2 out;
-        if ((dd & 1) == 0) {
-          out[0] = (row[0][w] & 0xffffu) | (row[1][w] << 16);
-          out[1] = (row[2][w] & 0xffffu) | (row[3][w] << 16);
-        } else {
-          out[0] = (row[0][w] >> 16) | (row[1][w] & 0xffff0000u);
-          out[1] = (row[2][w] >> 16) | (row[3][w] & 0xffff0000u);
-        }
-        *reinterpret_cast<u32x2*>(s_vt + (8 * dg + dd) * VP + 4 * kg) = out;
-      }
-    }
-    __syncthreads();
-
-    // ---- wave-level classification ----
-    const int w_max = iw_last - j0, w_min = iw - (j0 + kBN - 1);
-    const bool w_live = wave_live && w_max >= 0;
-    if (w_live) {
-      const bool w_loc = (w0 > 0) && (w_min < w0);
-      const bool w_rem = w_max >= w0;
-      const bool all_rem = w_min >= w0;
-      const bool all_loc = (w_min >= 0) && (w_max < w0);
-      f32x16 s[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb][0] = s[kb][1] = f32x16{};
-
-      const uint16_t* kfirst = w_rem ? s_krem : s_kloc;
+    if (masked) {
+      // i - j = t - rc(r) with t a per-lane, per-tile value and rc(r) = 8(r/4) + r%4 a
+      // compile-time row constant: each test compares a constant with one tile threshold.
+      const int t0 = iw + col - j0 - 4 * h;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(kfirst + (32 * kb + col) * KP + 16 * c + 8 * h);
-          if (w_rem) {
-            s[kb][0] = mfma32(av, qr[0][c], s[kb][0]);
-            s[kb][1] = mfma32(av, qr[1][c], s[kb][1]);
-          } else {
-            s[kb][0] = mfma32(av, qt[0][c], s[kb][0]);
-            s[kb][1] = mfma32(av, qt[1][c], s[kb][1]);
-          }
-        }
-
-      // Band tile holding both kinds of pair: add the base scores and route by index.
-      if (w_loc && w_rem) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            f32x16 t = f32x16{};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              const u32x4 av = *reinterpret_cast<const u32x4*>(s_kloc + (32 * kb + col) * KP + 16 * c + 8 * h);
-              t = mfma32(av, qt[qb][c], t);
-            }
-            const int i = iw + 32 * qb + col;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rel = i - (j0 + 32 * kb + c_row(r, h));
-              if (rel < w0) s[kb][qb][r] = t[r];
-            }
-          }
-      }
-
-      // ---- online softmax (scores in log2 units), local and remote sums kept apart ----
-      u32x4 pb[2][2][2];  // [qb][kb][chunk]
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int i = iw + 32 * qb + col;
-        float mx = kNegBig;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int qb = 0; qb < 2; ++qb) {
+          const int t = t0 + 32 * qb - 32 * kb;
+          const int keep_le = t - lo_rel;  // i - j >= lo_rel  <=>  rc <= keep_le
+          const int drop_le = t - w0;      // i - j <  w0      <=>  rc >  drop_le
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float x = s[kb][qb][r] * a.scale_log2;
-            if (!(all_rem || all_loc)) {
-              const int rel = i - (j0 + 32 * kb + c_row(r, h));
-              if (rel < 0) x = kNegBig;
-            }
-            s[kb][qb][r] = x;
-            mx = fmaxf(mx, x);
+            const int rc = 8 * (r >> 2) + (r & 3);
+            const bool keep = (rc <= keep_le) && (!local_pass || rc > drop_le);
+            if (!keep) s[kb][qb][r] = kNegBig;
           }
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m_run[qb], mx);
+        }
+    }
+    u32x4 pb[2][2][2];  // [qb][kb][chunk] bf16 P^T operands
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = kNegBig;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[kb][qb][r], s[kb][qb][r + 1]);
+      mx = pair_max(mx);
+      const bool up = mx > m_run[qb] + kSlack;
+      if (wave_any(up)) {
+        const float m_new = up ? mx : m_run[qb];
         const float alpha = fast_exp2(m_run[qb] - m_new);
         m_run[qb] = m_new;
-        l_loc[qb] *= alpha;
-        l_rem[qb] *= alpha;
+        l_pass[0][qb] *= alpha;
+        l_pass[1][qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db][qb] *= alpha;
-        float sl = 0.f, sr = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv = fast_exp2(s[kb][qb][r] - m_new);
-            s[kb][qb][r] = pv;
-            if (all_rem) {
-              sr += pv;
-            } else if (all_loc) {
-              sl += pv;
-            } else {
-              const int rel = i - (j0 + 32 * kb + c_row(r, h));
-              if (rel >= w0) sr += pv; else sl += pv;
-            }
-          }
-#pragma unroll
-          for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-              pb[qb][kb][ch][w] = pack_bf16x2(s[kb][qb][8 * ch + 2 * w], s[kb][qb][8 * ch + 2 * w + 1]);
-        }
-        l_loc[qb] += sl;
-        l_rem[qb] += sr;
       }
-
-      // ---- O^T += V^T P^T ----
+      const float m_use = m_run[qb];
+      float ps = 0.f;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-          for (int ch = 0; ch < 2; ++ch) {
-            const uint16_t* vr = s_vt + (32 * db + col) * VP + 32 * kb + 16 * ch + 4 * h;
-            const u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
-            const u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 8);
-            const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
-            o[db][0] = mfma32(av, pb[0][kb][ch], o[db][0]);
-            o[db][1] = mfma32(av, pb[1][kb][ch], o[db][1]);
+          for (int w = 0; w < 4; ++w) {
+            const int r = 8 * ch + 2 * w;
+            const uint32_t pk = pack_bf16x2(fast_exp2(s[kb][qb][r] - m_use), fast_exp2(s[kb][qb][r + 1] - m_use));
+            pb[qb][kb][ch][w] = pk;
+            ps = sum_bf16x2(pk, ps);
           }
+      l_pass[pass][qb] += ps;
     }
+    const uint16_t* vs = s_v[buf];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        const int key = 32 * kb + 16 * ch + tr_key;
+        const uint16_t* r0 = vs + key * D;
+        const uint16_t* r1 = vs + (key + 8) * D;
+        const int sw0 = swz(key), sw1 = swz(key + 8);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int d = 32 * db + tr_d;
+          const u32x2 v0 = read_tr(r0 + 8 * ((d >> 3) ^ sw0) + (d & 7));
+          const u32x2 v1 = read_tr(r1 + 8 * ((d >> 3) ^ sw1) + (d & 7));
+          const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
+          o[db][0] = mfma32(av, pb[0][kb][ch], o[db][0]);
+          o[db][1] = mfma32(av, pb[1][kb][ch], o[db][1]);
+        }
+      }
+  };
+
+  // ---------------- pass A: local pairs, tiles n_kt-1 down to kt_lo ----------------
+  const int n_kt = i_last / kBN + 1;
+  const int kt_lo = max(0, i0 - w0 + 1) / kBN;  // first tile with a local pair of this workgroup
+  if (w0 > 0) {
+    u32x4 qt[2][NC];
+    load_q(false, qt);
+    stage_direct(kbase, s_k[0], (n_kt - 1) * kBN);
+    stage_direct(vbase, s_v[0], (n_kt - 1) * kBN);
+    wait_loads();
     __syncthreads();
+    int buf = 0;
+    for (int kt = n_kt - 1; kt >= kt_lo; --kt) {
+      const int j0 = kt * kBN;
+      if (kt - 1 >= kt_lo) {
+        stage_direct(kbase, s_k[buf ^ 1], j0 - kBN);
+        stage_direct(vbase, s_v[buf ^ 1], j0 - kBN);
+      }
+      const int w_max = iw_last - j0, w_min = iw - (j0 + kBN - 1);
+      if (wave_live && w_max >= 0 && w_min < w0) {
+        const bool masked = !(w_min >= 0 && w_max < w0);
+        tile_step(buf, qt, j0, masked, 0, true);
+      }
+      wait_loads();
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // ---------------- pass R: remote pairs, tiles kt_hi-1 down to 0 ----------------
+  if constexpr (kBif) {
+    const int kt_hi = (i_last >= w0) ? (i_last - w0) / kBN + 1 : 0;  // tiles holding a remote pair
+    if (kt_hi > 0) {
+      u32x4 qr[2][NC];
+      load_q(true, qr);
+      const uint16_t* rbase = a.krot + kv_off;
+      auto stage_r = [&](int kt, int bf, Staged<D>& st) __attribute__((always_inline)) {
+        if constexpr (MODE == kPrerotated) {
+          stage_direct(rbase, s_k[bf], kt * kBN);
+        } else {
+          fetch_k(kt, st);
+        }
+        stage_direct(vbase, s_v[bf], kt * kBN);
+      };
+      {
+        Staged<D> st;
+        stage_r(kt_hi - 1, 0, st);
+        if constexpr (MODE == kFused) commit_k(kt_hi - 1, s_k[0], st);
+      }
+      wait_loads();
+      __syncthreads();
+      int buf = 0;
+      for (int kt = kt_hi - 1; kt >= 0; --kt) {
+        const int j0 = kt * kBN;
+        Staged<D> st;
+        if (kt - 1 >= 0) stage_r(kt - 1, buf ^ 1, st);
+        const int w_max = iw_last - j0, w_min = iw - (j0 + kBN - 1);
+        if (wave_live && w_max >= w0) {
+          const bool masked = w_min < w0;
+          tile_step(buf, qr, j0, masked, w0, false);
+        }
+        if constexpr (MODE == kFused) {
+          if (kt - 1 >= 0) commit_k(kt - 1, s_k[buf ^ 1], st);
+        }
+        wait_loads();
+        __syncthreads();
+        buf ^= 1;
+      }
+    }
   }
 
   // ---- epilogue: LSE merge of the local and remote weights, normalise, store ----
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int i = iw + 32 * qb + col;
-    const float w_a = pair_sum(l_loc[qb]);  // local (pass A) weight, relative to 2^m
-    const float w_r = pair_sum(l_rem[qb]);  // remote (pass B minus pass C) weight
+    const float w_a = pair_sum(l_pass[0][qb]);  // local (pass A) weight, relative to 2^m
+    const float w_r = pair_sum(l_pass[1][qb]);  // remote (pass B minus pass C) weight
     const float den = w_a + w_r;
     const float inv = 1.0f / den;
     if (i < L) {
@@ -334,11 +429,34 @@ void prefill_kernel(const PrefillArgs<D> a) {
   }
 }
 
+// K' = R(Delta_j) K~ for every key row (prerotated mode): one thread per 8 rotation pairs.
+template <int D>
+__global__ __launch_bounds__(256) void rotate_keys_kernel(const uint16_t* __restrict__ k, uint16_t* __restrict__ kr,
+                                                          long long n_rows, int Hkv, int L, int G,
+                                                          const PrefillArgs<D> a) {
+  constexpr int HALF = D / 2, MCH = HALF / 8;
+  const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (u >= n_rows * MCH) return;
+  const long long row = u / MCH;  // row = (b * L + j) * Hkv + g
+  const int m = (int)(u % MCH);
+  const int j = (int)((row / Hkv) % L);
+  const size_t off = (size_t)row * D + 8 * m;
+  u32x4 lo = *reinterpret_cast<const u32x4*>(k + off);
+  u32x4 hi = *reinterpret_cast<const u32x4*>(k + off + HALF);
+  uint32_t w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = a.W[8 * m + e];
+  rotate8(lo, hi, correction_offset(j, G), w);
+  *reinterpret_cast<u32x4*>(kr + off) = lo;
+  *reinterpret_cast<u32x4*>(kr + off + HALF) = hi;
+}
+
 template <int D>
 static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
   PrefillArgs<D> a;
   a.q = static_cast<const uint16_t*>(p.q);
   a.k = static_cast<const uint16_t*>(p.k);
+  a.krot = static_cast<const uint16_t*>(p.krot);
   a.v = static_cast<const uint16_t*>(p.v);
   a.o = static_cast<uint16_t*>(p.o);
   a.lse = p.lse;
@@ -357,7 +475,21 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
   for (int i = 0; i < D / 2; ++i) a.W[i] = p.W[i];
   const long long nwg = (long long)p.batch * a.n_units * a.n_tiles;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  // With every pair local (w0 == L, which the host also sets for G == 1) there is no remote
+  // key: plain causal attention with no rotation at all.
+  if (p.w0 >= p.L) {
+    hipLaunchKernelGGL((prefill_kernel<D, kLocalOnly>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  } else if (p.krot != nullptr) {
+    const long long rows = (long long)p.batch * p.L * p.n_kv_heads;
+    const long long units = rows * (D / 16);
+    hipLaunchKernelGGL(rotate_keys_kernel<D>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, a.k,
+                       static_cast<uint16_t*>(p.krot), rows, p.n_kv_heads, p.L, p.G, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill_kernel<D, kPrerotated>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<D, kFused>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -365,6 +497,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream) {
   if (p.head_dim == 128) return launch_prefill_d<128>(p, stream);
   if (p.head_dim == 64) return launch_prefill_d<64>(p, stream);
   return hipErrorInvalidValue;
+}
+
+size_t prefill_workspace_bytes(long long batch, long long L, int n_kv_heads, int head_dim) {
+  return static_cast<size_t>(batch * L * n_kv_heads * head_dim * 2);
 }
 
 }  // namespace bifocal
