@@ -9,11 +9,12 @@
 // summary, Methodologie section 2 (correction rotation by additive composition; the merge
 // reaches the exact routing output with no mask matrix, stabilised by log-sum-exp).
 //
-// Inclusion-exclusion in registers: pass B minus pass C is exactly the set of remote pairs,
-// so the kernel routes each score by its index (no mask matrix) and accumulates local and
-// remote contributions against one running max into one numerator, keeping the local (A)
-// and remote (B - C) weights as separate per-row sums; the epilogue merges them by LSE.
-// Nothing is subtracted, so there is no cancellation when W_C is close to W_B.
+// Inclusion-exclusion in registers: a local pass (pass A: base scores on pairs with
+// 0 <= i-j < w0) and a remote pass (pass B minus pass C: aliased scores on pairs with
+// i-j >= w0) run over the key tiles against one running max and one numerator. Each pair is
+// scored in exactly one pass (the other masks it by index, no mask matrix), the two passes
+// keep separate weight sums W_A and W_B - W_C, and the epilogue merges them by LSE. Nothing
+// is subtracted, so there is no cancellation when W_C is close to W_B.
 //
 // Key correction rotation K' = R(Delta_j) K~, two modes:
 //   fused       -- rotated per key tile while the tile is staged into LDS (no workspace);
@@ -23,16 +24,19 @@
 //                  VALU-bound loop, so the prerotated mode is the fast one on CDNA4.
 //
 // Work decomposition
-//   workgroup = 256 threads = 4 waves (one per SIMD); one KV head, BM query positions, hpw
-//   query heads (hpw = 4 for the 4:1 GQA of Qwen3-4B/8B, so all four heads share each staged
-//   K/V tile). wave = one query head x 64 query rows (two 32-column MFMA blocks).
-//   key tile = 64 keys; K' (tiles with remote pairs), K~ (tiles with local pairs) and V^T are
-//   double-buffered in LDS; tile kt+1 is fetched into registers while tile kt is computed.
+//   workgroup = 512 threads = 8 waves, two per SIMD, so one wave's softmax (VALU) overlaps
+//   the other wave's MFMAs. One KV head, BM query positions, hpw query heads: with the 4:1
+//   GQA of Qwen3-4B/8B, hpw = 4 and BM = 64, so all four heads share each staged K/V tile.
+//   wave = one query head x 32 query rows (one 32-column MFMA block).
+//   key tile = 64 keys. K (K~ in pass A, K' in pass R) and V are double-buffered in LDS,
+//   filled by global_load_lds_dwordx4 (no registers, no VALU) into an XOR-swizzled layout;
+//   tile kt-1 is in flight while tile kt is computed.
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query column, so the row max
 //   and sum are in-lane plus one v_permlane32_swap; P^T feeds the PV MFMA from registers;
-//   O^T = V^T P^T accumulates in 128 registers per lane. Q is pre-scaled by log2(e)/sqrt(D),
-//   so scores arrive in log2 units. The running max is only raised when a tile's max exceeds
-//   it by more than kSlack (the output is rescaled then); otherwise exponents stay <= kSlack.
+//   the V^T operand comes from ds_read_b64_tr_b16 on the row-major V tile; O^T accumulates
+//   in 64 registers per lane. Q is pre-scaled by log2(e)/sqrt(D), so scores arrive in log2
+//   units. The running max is only raised when a tile's max exceeds it by more than kSlack
+//   (the output is rescaled then); otherwise exponents stay <= kSlack.
 //   Workgroup ids are remapped so that each of the 8 XCDs owns a contiguous range of
 //   (batch, head unit, query tile) work, longest causal rows first.
 #include "device_common.hpp"
@@ -59,6 +63,8 @@ struct PrefillArgs {
 };
 
 constexpr int kBN = 64;         // keys per tile
+constexpr int kWaves = 8;       // waves per workgroup (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
 constexpr float kSlack = 8.0f;  // log2 units a row max may run ahead of the stored max
 
 template <int D>
@@ -68,23 +74,22 @@ struct Tile {
   static constexpr int NDB = D / 32;       // 32-row d blocks of O^T
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;     // rows per wave-wide 1 KB direct load
-  static constexpr int NLD = kBN / RPI / 4;  // direct loads per wave per tile (4 waves)
+  static constexpr int NLDW = kBN / RPI / kWaves;  // direct loads per wave per tile
   static constexpr int MCH = HALF / 8;     // 8-pair chunks per half row
-  static constexpr int KREP = kBN * MCH / 256;  // fused-mode K staging units per thread
   static constexpr int TSZ = kBN * D;      // elements per tile (rows are unpadded)
 };
 
-// Key/value tiles are stored row-major with 16-byte chunk `c` of row `r` at position
-// c ^ swz(r). swz permutes 0..7 so that (a) 8 consecutive rows read at one chunk (the K
-// operand, ds_read_b128) hit 8 distinct bank groups and (b) 4 consecutive rows read at a
-// chunk pair (the transposed V operand, ds_read_b64_tr_b16) hit 4 distinct pairs.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
-
-// Fused mode: registers holding the key rows a thread rotates on their way to LDS.
+// Key/value tiles are row-major with 16-byte chunk c of row r stored at position c ^ swz(r).
+// LDS has 64 four-byte banks, i.e. one 256-byte line. D = 128 (one row per line): swz(r) is a
+// 4-bit permutation of r mod 16, so 16 consecutive rows read at one chunk (the K operand,
+// ds_read_b128, 16 lanes per cycle) hit 16 distinct bank groups, and 4 consecutive rows read
+// at chunks 0..3 (the transposed V operand, ds_read_b64_tr_b16, 32 lanes per cycle) hit
+// disjoint groups. D = 64 (two rows per line): the same two properties per row parity.
 template <int D>
-struct Staged {
-  u32x4 rlo[Tile<D>::KREP], rhi[Tile<D>::KREP];  // key halves (d < D/2, d >= D/2)
-};
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 #define LDS_AS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -108,14 +113,8 @@ __device__ __forceinline__ float max3f(float a, float b, float c) { return __bui
 // bifocal with the key rotation done while staging (fused) or read from a workspace.
 enum PrefillMode { kLocalOnly = 0, kFused = 1, kPrerotated = 2 };
 
-// Two passes over the key tiles of a query tile, sharing one running max and one numerator:
-//   pass A (local):  tiles holding pairs with 0 <= i-j < w0, base scores q~ . k~, weight W_A;
-//   pass R (remote): tiles holding pairs with i-j >= w0, aliased scores q' . k', weight W_B - W_C.
-// Each pair is scored in exactly one pass (the other pass masks it by index), so the sum of the
-// two passes is the inclusion-exclusion merge with no subtraction. Pass A runs first, from the
-// diagonal down; only one of q~ / q' is held in registers at a time.
 template <int D, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(const PrefillArgs<D> a) {
   using T = Tile<D>;
   constexpr int HALF = T::HALF, NC = T::NC, NDB = T::NDB, CPR = T::CPR, RPI = T::RPI, MCH = T::MCH;
@@ -140,47 +139,44 @@ void prefill_kernel(const PrefillArgs<D> a) {
   const int upk = Hg / a.hpw;
   const int kvh = unit / upk;
   const int head = kvh * Hg + (unit % upk) * a.hpw + (wave % a.hpw);
-  const int BM = 64 * (4 / a.hpw);
+  const int BM = 32 * (kWaves / a.hpw);
   const int i0 = tile * BM;
-  const int iw = i0 + (wave / a.hpw) * 64;
+  const int iw = i0 + 32 * (wave / a.hpw);  // this wave's 32 query rows
   const int L = a.L, w0 = a.w0, G = a.G;
   const float qscale = a.scale_log2;
 
-  for (int t = tid; t < HALF; t += 256) s_w[t] = a.W[t];
+  for (int t = tid; t < HALF; t += kThreads) s_w[t] = a.W[t];
   __syncthreads();
 
   const size_t q_row_stride = (size_t)a.Hq * D;
-  // Query operand (B of S^T = K Q^T): lane (col, h) of row block qb holds q[i][16c + 8h .. +8],
-  // scaled into log2 units; with `rotate` the correction rotation R(Delta_i) is applied first.
-  auto load_q = [&](bool rotate, u32x4 (&dst)[2][NC]) {
+  const int qi = iw + col;  // this lane's query row
+  // Query operand (B of S^T = K Q^T): lane (col, h) holds q[qi][16c + 8h .. +8], scaled into
+  // log2 units; with `rotate` the correction rotation R(Delta_qi) is applied first.
+  auto load_q = [&](bool rotate, u32x4 (&dst)[NC]) __attribute__((always_inline)) {
+    const uint16_t* src = a.q + ((size_t)b * L + qi) * q_row_stride + (size_t)head * D + 8 * h;
+    u32x4 raw[NC];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int i = iw + 32 * qb + col;
-      const uint16_t* src = a.q + ((size_t)b * L + i) * q_row_stride + (size_t)head * D + 8 * h;
-      u32x4 raw[NC];
+    for (int c = 0; c < NC; ++c) {
+      raw[c] = u32x4{0, 0, 0, 0};
+      if (qi < L) raw[c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+    }
+    if (rotate) {
+      const int dq = correction_offset(qi < L ? qi : 0, G);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        raw[c] = u32x4{0, 0, 0, 0};
-        if (i < L) raw[c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+      for (int c = 0; c < NC / 2; ++c) {
+        u32x4 lo = raw[c], hi = raw[c + NC / 2];
+        rotate8_scaled(lo, hi, dq, &s_w[16 * c + 8 * h], qscale);
+        dst[c] = lo;
+        dst[c + NC / 2] = hi;
       }
-      if (rotate) {
-        const int dq = correction_offset(i < L ? i : 0, G);
+    } else {
 #pragma unroll
-        for (int c = 0; c < NC / 2; ++c) {
-          u32x4 lo = raw[c], hi = raw[c + NC / 2];
-          rotate8_scaled(lo, hi, dq, &s_w[16 * c + 8 * h], qscale);
-          dst[qb][c] = lo;
-          dst[qb][c + NC / 2] = hi;
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) dst[qb][c] = scale8(raw[c], qscale);
-      }
+      for (int c = 0; c < NC; ++c) dst[c] = scale8(raw[c], qscale);
     }
   };
 
   const int i_last = min(i0 + BM, L) - 1;
-  const int iw_last = min(iw + 63, L - 1);
+  const int iw_last = min(iw + 31, L - 1);
   const bool wave_live = iw <= L - 1;
   const size_t kv_row_stride = (size_t)a.Hkv * D;
   const size_t kv_off = (size_t)b * L * kv_row_stride + (size_t)kvh * D;
@@ -188,244 +184,213 @@ void prefill_kernel(const PrefillArgs<D> a) {
   const uint16_t* vbase = a.v + kv_off;
 
   // ---- staging ----
-  // Direct loads: wave w fills rows RPI*(NLD*w + n) + lane/CPR, lane slot lane%CPR, which holds
-  // global chunk (slot ^ swz(row)) of that row. Rows past L are clamped to L-1: their scores
-  // are masked (j > i) and their weights are 0.
-  const int ld_row0 = RPI * T::NLD * wave + lane / CPR;
+  // Direct loads: wave w fills rows RPI*(NLDW*w + n) + lane/CPR; lane slot p = lane%CPR holds
+  // global chunk p ^ swz(row). Rows past L are clamped to L-1: their scores are masked
+  // (j > i) and their weights are 0.
+  const int ld_row0 = RPI * T::NLDW * wave + lane / CPR;
   const int ld_slot = lane % CPR;
-  auto stage_direct = [&](const uint16_t* src, uint16_t* tile, int j0) __attribute__((always_inline)) {
+  auto stage_direct = [&](const uint16_t* src, uint16_t* tile_lds, int j0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int n = 0; n < T::NLD; ++n) {
+    for (int n = 0; n < T::NLDW; ++n) {
       const int row = ld_row0 + RPI * n;
       const int j = min(j0 + row, L - 1);
-      const int chunk = ld_slot ^ swz(row);
-      load_lds16(src + (size_t)j * kv_row_stride + 8 * chunk, tile + (RPI * T::NLD * wave + RPI * n) * D);
+      load_lds16(src + (size_t)j * kv_row_stride + 8 * (ld_slot ^ swz<D>(row)),
+                 tile_lds + (RPI * T::NLDW * wave + RPI * n) * D);
     }
   };
-  // Fused mode: thread -> (key, 8-pair chunk) units, rotated in registers, written swizzled.
-  const int m_chunk = tid % MCH;
-  auto fetch_k = [&](int kt, Staged<D>& st) __attribute__((always_inline)) {
-    const int j0 = kt * kBN;
-#pragma unroll
-    for (int rep = 0; rep < T::KREP; ++rep) {
-      const int j = min(j0 + (tid + 256 * rep) / MCH, L - 1);
-      const uint16_t* src = kbase + (size_t)j * kv_row_stride + 8 * m_chunk;
-      st.rlo[rep] = *reinterpret_cast<const u32x4*>(src);
-      st.rhi[rep] = *reinterpret_cast<const u32x4*>(src + HALF);
+  // Fused mode: thread -> (key, 8-pair chunk) unit, rotated in registers, written swizzled.
+  const int f_key = tid / MCH, f_chunk = tid % MCH;
+  const bool f_unit = tid < kBN * MCH;
+  auto fetch_k = [&](int j0, u32x4& lo, u32x4& hi) __attribute__((always_inline)) {
+    lo = hi = u32x4{0, 0, 0, 0};
+    if (f_unit) {
+      const int j = min(j0 + f_key, L - 1);
+      const uint16_t* src = kbase + (size_t)j * kv_row_stride + 8 * f_chunk;
+      lo = *reinterpret_cast<const u32x4*>(src);
+      hi = *reinterpret_cast<const u32x4*>(src + HALF);
     }
   };
-  auto commit_k = [&](int kt, uint16_t* tile, Staged<D>& st) __attribute__((always_inline)) {
-    const int j0 = kt * kBN;
-#pragma unroll
-    for (int rep = 0; rep < T::KREP; ++rep) {
-      const int key = (tid + 256 * rep) / MCH;
-      u32x4 lo = st.rlo[rep], hi = st.rhi[rep];
-      rotate8(lo, hi, correction_offset(j0 + key, G), &s_w[8 * m_chunk]);
-      uint16_t* row = tile + key * D;
-      *reinterpret_cast<u32x4*>(row + 8 * (m_chunk ^ swz(key))) = lo;
-      *reinterpret_cast<u32x4*>(row + 8 * ((m_chunk + MCH) ^ swz(key))) = hi;
+  auto commit_k = [&](int j0, uint16_t* tile_lds, u32x4 lo, u32x4 hi) __attribute__((always_inline)) {
+    if (f_unit) {
+      rotate8(lo, hi, correction_offset(j0 + f_key, G), &s_w[8 * f_chunk]);
+      uint16_t* row = tile_lds + f_key * D;
+      const int sw = swz<D>(f_key);
+      *reinterpret_cast<u32x4*>(row + 8 * (f_chunk ^ sw)) = lo;
+      *reinterpret_cast<u32x4*>(row + 8 * ((f_chunk + MCH) ^ sw)) = hi;
     }
   };
 
-  f32x16 o[NDB][2];
+  f32x16 o[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db][0] = o[db][1] = f32x16{};
-  float m_run[2] = {kNegBig, kNegBig};
-  float l_pass[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [pass: 0 local, 1 remote][qb]
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  float m_run = kNegBig;
+  float l_pass[2] = {0.f, 0.f};  // [pass: 0 local (W_A), 1 remote (W_B - W_C)]
 
-  // LDS offsets of this lane's operands inside a tile.
-  // K (A of S^T): row 32kb + col, chunk 2c + h.  V (A of O^T via the transposed read): group
-  // g = lane/16 covers d = 32db + 16(g%2) + 0..15 and keys 16ch + 4h + 0..3 (+8 for elements 4..7).
+  // Operand offsets inside a tile (elements). K (A of S^T): row 32kb + col, chunk 2c + h.
+  // V (A of O^T, transposed read): lanes of group g = lane/16 cover d = 32db + 16(g%2) + 0..15
+  // and keys 16ch + 4h + 0..3 (+8 for elements 4..7); lane r of the group names 4 values of
+  // row 16ch + 4h + r/4 (+8) at d = 32db + 16(g%2) + 4(r%4).
+  const int k_sw = swz<D>(col);
   const int tr_r = lane & 15;
   const int tr_key = 4 * h + (tr_r >> 2);
   const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_r & 3);
 
-  // One tile: S^T = K Q^T, optional index mask, online softmax (log2 units), O^T += V^T P^T.
-  // Kept pairs satisfy lo_rel <= i - j (and i - j < w0 in the local pass).
-  auto tile_step = [&](int buf, const u32x4 (&qa)[2][NC], int j0, bool masked, int lo_rel,
-                       bool local_pass) __attribute__((always_inline)) {
-    const int pass = local_pass ? 0 : 1;
-    f32x16 s[2][2];
-    const uint16_t* ks = s_k[buf];
+  // One tile: S^T = K Q^T, index mask (masked tiles only), online softmax in log2 units with a
+  // lazily raised max, O^T += V^T P^T. Kept pairs: lo_rel <= i - j (and i - j < w0 in pass A).
+  auto tile_step = [&](const uint16_t* ks, const uint16_t* vs, const u32x4 (&qa)[NC], int j0, bool masked,
+                       int lo_rel, bool local_pass) __attribute__((always_inline)) {
+    f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb][0] = s[kb][1] = f32x16{};
-      const int row = 32 * kb + col;
-      const uint16_t* krow = ks + row * D;
-      const int sw = swz(row);
+      s[kb] = f32x16{};
+      const uint16_t* krow = ks + (32 * kb + col) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * c + h) ^ sw));
-        s[kb][0] = mfma32(av, qa[0][c], s[kb][0]);
-        s[kb][1] = mfma32(av, qa[1][c], s[kb][1]);
+        const u32x4 av = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * c + h) ^ k_sw));
+        s[kb] = mfma32(av, qa[c], s[kb]);
       }
     }
     if (masked) {
-      // i - j = t - rc(r) with t a per-lane, per-tile value and rc(r) = 8(r/4) + r%4 a
-      // compile-time row constant: each test compares a constant with one tile threshold.
-      const int t0 = iw + col - j0 - 4 * h;
+      // i - j = t - rc(r) with t per lane and tile, rc(r) = 8(r/4) + r%4 a compile-time row
+      // constant: each test compares a constant with one threshold.
+      const int t0 = qi - j0 - 4 * h;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const int t = t0 - 32 * kb;
+        const int keep_le = t - lo_rel;  // i - j >= lo_rel  <=>  rc <= keep_le
+        const int drop_le = t - w0;      // i - j <  w0      <=>  rc >  drop_le
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int t = t0 + 32 * qb - 32 * kb;
-          const int keep_le = t - lo_rel;  // i - j >= lo_rel  <=>  rc <= keep_le
-          const int drop_le = t - w0;      // i - j <  w0      <=>  rc >  drop_le
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rc = 8 * (r >> 2) + (r & 3);
-            const bool keep = (rc <= keep_le) && (!local_pass || rc > drop_le);
-            if (!keep) s[kb][qb][r] = kNegBig;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int rc = 8 * (r >> 2) + (r & 3);
+          const bool keep = (rc <= keep_le) && (!local_pass || rc > drop_le);
+          if (!keep) s[kb][r] = kNegBig;
         }
-    }
-    u32x4 pb[2][2][2];  // [qb][kb][chunk] bf16 P^T operands
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = kNegBig;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[kb][qb][r], s[kb][qb][r + 1]);
-      mx = pair_max(mx);
-      const bool up = mx > m_run[qb] + kSlack;
-      if (wave_any(up)) {
-        const float m_new = up ? mx : m_run[qb];
-        const float alpha = fast_exp2(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_pass[0][qb] *= alpha;
-        l_pass[1][qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db][qb] *= alpha;
       }
-      const float m_use = m_run[qb];
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int r = 8 * ch + 2 * w;
-            const uint32_t pk = pack_bf16x2(fast_exp2(s[kb][qb][r] - m_use), fast_exp2(s[kb][qb][r + 1] - m_use));
-            pb[qb][kb][ch][w] = pk;
-            ps = sum_bf16x2(pk, ps);
-          }
-      l_pass[pass][qb] += ps;
     }
-    const uint16_t* vs = s_v[buf];
+    float mx = kNegBig;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[kb][r], s[kb][r + 1]);
+    mx = pair_max(mx);
+    const bool up = mx > m_run + kSlack;
+    if (wave_any(up)) {
+      const float m_new = up ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_pass[0] *= alpha;
+      l_pass[1] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    }
+    u32x4 pb[2][2];  // [kb][chunk] bf16 P^T operands
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int r = 8 * ch + 2 * w;
+          const uint32_t pk = pack_bf16x2(fast_exp2(s[kb][r] - m_run), fast_exp2(s[kb][r + 1] - m_run));
+          pb[kb][ch][w] = pk;
+          ps = sum_bf16x2(pk, ps);
+        }
+    l_pass[local_pass ? 0 : 1] += ps;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
-        const int key = 32 * kb + 16 * ch + tr_key;
-        const uint16_t* r0 = vs + key * D;
-        const uint16_t* r1 = vs + (key + 8) * D;
-        const int sw0 = swz(key), sw1 = swz(key + 8);
+        const int key0 = 32 * kb + 16 * ch + tr_key, key1 = key0 + 8;
+        const uint16_t* r0 = vs + key0 * D;
+        const uint16_t* r1 = vs + key1 * D;
+        const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int d = 32 * db + tr_d;
           const u32x2 v0 = read_tr(r0 + 8 * ((d >> 3) ^ sw0) + (d & 7));
           const u32x2 v1 = read_tr(r1 + 8 * ((d >> 3) ^ sw1) + (d & 7));
-          const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
-          o[db][0] = mfma32(av, pb[0][kb][ch], o[db][0]);
-          o[db][1] = mfma32(av, pb[1][kb][ch], o[db][1]);
+          o[db] = mfma32(u32x4{v0[0], v0[1], v1[0], v1[1]}, pb[kb][ch], o[db]);
         }
       }
+  };
+
+  // One pass over n tiles kt = kt_first, kt_first-1, ..., with tile t+1 in flight while tile t
+  // is computed. `active`: this wave has pairs of the pass in the tile; `masked`: some pair of
+  // the tile needs the index mask.
+  auto run_pass = [&](int kt_first, int n, const u32x4 (&qa)[NC], const uint16_t* ksrc, bool rotate_k,
+                      bool local_pass, int lo_rel) __attribute__((always_inline)) {
+    auto j0_of = [&](int t) { return (kt_first - t) * kBN; };
+    u32x4 flo, fhi;
+    if (rotate_k) {
+      fetch_k(j0_of(0), flo, fhi);
+      commit_k(j0_of(0), s_k[0], flo, fhi);
+    } else {
+      stage_direct(ksrc, s_k[0], j0_of(0));
+    }
+    stage_direct(vbase, s_v[0], j0_of(0));
+    wait_loads();
+    __syncthreads();
+    for (int t = 0; t < n; ++t) {
+      const int buf = t & 1;
+      const bool more = t + 1 < n;
+      if (more) {
+        if (rotate_k) fetch_k(j0_of(t + 1), flo, fhi);
+        else stage_direct(ksrc, s_k[buf ^ 1], j0_of(t + 1));
+        stage_direct(vbase, s_v[buf ^ 1], j0_of(t + 1));
+      }
+      const int j0 = j0_of(t);
+      const int w_max = iw_last - j0, w_min = iw - (j0 + kBN - 1);
+      const bool active = wave_live && (local_pass ? (w_max >= 0 && w_min < w0) : (w_max >= w0));
+      if (active) {
+        const bool masked = local_pass ? !(w_min >= 0 && w_max < w0) : (w_min < w0);
+        if (masked) tile_step(s_k[buf], s_v[buf], qa, j0, true, lo_rel, local_pass);
+        else tile_step(s_k[buf], s_v[buf], qa, j0, false, lo_rel, local_pass);
+      }
+      if (more && rotate_k) commit_k(j0_of(t + 1), s_k[buf ^ 1], flo, fhi);
+      wait_loads();
+      __syncthreads();
+    }
   };
 
   // ---------------- pass A: local pairs, tiles n_kt-1 down to kt_lo ----------------
   const int n_kt = i_last / kBN + 1;
   const int kt_lo = max(0, i0 - w0 + 1) / kBN;  // first tile with a local pair of this workgroup
   if (w0 > 0) {
-    u32x4 qt[2][NC];
+    u32x4 qt[NC];
     load_q(false, qt);
-    stage_direct(kbase, s_k[0], (n_kt - 1) * kBN);
-    stage_direct(vbase, s_v[0], (n_kt - 1) * kBN);
-    wait_loads();
-    __syncthreads();
-    int buf = 0;
-    for (int kt = n_kt - 1; kt >= kt_lo; --kt) {
-      const int j0 = kt * kBN;
-      if (kt - 1 >= kt_lo) {
-        stage_direct(kbase, s_k[buf ^ 1], j0 - kBN);
-        stage_direct(vbase, s_v[buf ^ 1], j0 - kBN);
-      }
-      const int w_max = iw_last - j0, w_min = iw - (j0 + kBN - 1);
-      if (wave_live && w_max >= 0 && w_min < w0) {
-        const bool masked = !(w_min >= 0 && w_max < w0);
-        tile_step(buf, qt, j0, masked, 0, true);
-      }
-      wait_loads();
-      __syncthreads();
-      buf ^= 1;
-    }
+    run_pass(n_kt - 1, n_kt - kt_lo, qt, kbase, false, true, 0);
   }
 
   // ---------------- pass R: remote pairs, tiles kt_hi-1 down to 0 ----------------
   if constexpr (kBif) {
     const int kt_hi = (i_last >= w0) ? (i_last - w0) / kBN + 1 : 0;  // tiles holding a remote pair
     if (kt_hi > 0) {
-      u32x4 qr[2][NC];
+      u32x4 qr[NC];
       load_q(true, qr);
-      const uint16_t* rbase = a.krot + kv_off;
-      auto stage_r = [&](int kt, int bf, Staged<D>& st) __attribute__((always_inline)) {
-        if constexpr (MODE == kPrerotated) {
-          stage_direct(rbase, s_k[bf], kt * kBN);
-        } else {
-          fetch_k(kt, st);
-        }
-        stage_direct(vbase, s_v[bf], kt * kBN);
-      };
-      {
-        Staged<D> st;
-        stage_r(kt_hi - 1, 0, st);
-        if constexpr (MODE == kFused) commit_k(kt_hi - 1, s_k[0], st);
-      }
-      wait_loads();
-      __syncthreads();
-      int buf = 0;
-      for (int kt = kt_hi - 1; kt >= 0; --kt) {
-        const int j0 = kt * kBN;
-        Staged<D> st;
-        if (kt - 1 >= 0) stage_r(kt - 1, buf ^ 1, st);
-        const int w_max = iw_last - j0, w_min = iw - (j0 + kBN - 1);
-        if (wave_live && w_max >= w0) {
-          const bool masked = w_min < w0;
-          tile_step(buf, qr, j0, masked, w0, false);
-        }
-        if constexpr (MODE == kFused) {
-          if (kt - 1 >= 0) commit_k(kt - 1, s_k[buf ^ 1], st);
-        }
-        wait_loads();
-        __syncthreads();
-        buf ^= 1;
-      }
+      if constexpr (MODE == kPrerotated) run_pass(kt_hi - 1, kt_hi, qr, a.krot + kv_off, false, false, w0);
+      else run_pass(kt_hi - 1, kt_hi, qr, kbase, true, false, w0);
     }
   }
 
   // ---- epilogue: LSE merge of the local and remote weights, normalise, store ----
+  const float w_a = pair_sum(l_pass[0]);  // local (pass A) weight, relative to 2^m
+  const float w_r = pair_sum(l_pass[1]);  // remote (pass B minus pass C) weight
+  const float den = w_a + w_r;
+  const float inv = 1.0f / den;
+  if (qi < L) {
+    uint16_t* dst = a.o + ((size_t)b * L + qi) * q_row_stride + (size_t)head * D;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int i = iw + 32 * qb + col;
-    const float w_a = pair_sum(l_pass[0][qb]);  // local (pass A) weight, relative to 2^m
-    const float w_r = pair_sum(l_pass[1][qb]);  // remote (pass B minus pass C) weight
-    const float den = w_a + w_r;
-    const float inv = 1.0f / den;
-    if (i < L) {
-      uint16_t* dst = a.o + ((size_t)b * L + i) * q_row_stride + (size_t)head * D;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 out;
-          out[0] = pack_bf16x2(o[db][qb][4 * g] * inv, o[db][qb][4 * g + 1] * inv);
-          out[1] = pack_bf16x2(o[db][qb][4 * g + 2] * inv, o[db][qb][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * g + 4 * h) = out;
-        }
-      if (a.lse != nullptr && h == 0)
-        a.lse[((size_t)b * a.Hq + head) * L + i] = (m_run[qb] + __log2f(den)) * 0.69314718055994531f;
-    }
+      for (int g = 0; g < 4; ++g) {
+        u32x2 out;
+        out[0] = pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+        out[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * g + 4 * h) = out;
+      }
+    if (a.lse != nullptr && h == 0)
+      a.lse[((size_t)b * a.Hq + head) * L + qi] = (m_run + __log2f(den)) * 0.69314718055994531f;
   }
 }
 
@@ -468,7 +433,7 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
   a.G = p.G;
   const int Hg = p.n_q_heads / p.n_kv_heads;
   a.hpw = (Hg % 4 == 0) ? 4 : (Hg % 2 == 0) ? 2 : 1;
-  const int BM = 64 * (4 / a.hpw);
+  const int BM = 32 * (kWaves / a.hpw);
   a.n_tiles = (p.L + BM - 1) / BM;
   a.n_units = p.n_q_heads / a.hpw;
   a.scale_log2 = p.scale_log2;
@@ -478,7 +443,7 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
   // With every pair local (w0 == L, which the host also sets for G == 1) there is no remote
   // key: plain causal attention with no rotation at all.
   if (p.w0 >= p.L) {
-    hipLaunchKernelGGL((prefill_kernel<D, kLocalOnly>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, kLocalOnly>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   } else if (p.krot != nullptr) {
     const long long rows = (long long)p.batch * p.L * p.n_kv_heads;
     const long long units = rows * (D / 16);
@@ -486,9 +451,9 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
                        static_cast<uint16_t*>(p.krot), rows, p.n_kv_heads, p.L, p.G, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_kernel<D, kPrerotated>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, kPrerotated>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<D, kFused>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, kFused>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
