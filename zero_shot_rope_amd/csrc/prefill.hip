@@ -120,8 +120,10 @@ void prefill_kernel(const PrefillArgs<D> a) {
   constexpr int HALF = T::HALF, NC = T::NC, NDB = T::NDB, CPR = T::CPR, RPI = T::RPI, MCH = T::MCH;
   constexpr bool kBif = MODE != kLocalOnly;
 
-  __shared__ __align__(16) uint16_t s_k[2][T::TSZ];
-  __shared__ __align__(16) uint16_t s_v[2][T::TSZ];
+  // Separate objects per buffer (not one indexed array), so the compiler can tell the tile
+  // being read from the tile whose direct loads are in flight and does not wait for them.
+  __shared__ __align__(16) uint16_t s_k0[T::TSZ], s_k1[T::TSZ];
+  __shared__ __align__(16) uint16_t s_v0[T::TSZ], s_v1[T::TSZ];
   __shared__ uint32_t s_w[HALF];
 
   const int tid = threadIdx.x;
@@ -316,41 +318,47 @@ void prefill_kernel(const PrefillArgs<D> a) {
   };
 
   // One pass over n tiles kt = kt_first, kt_first-1, ..., with tile t+1 in flight while tile t
-  // is computed. `active`: this wave has pairs of the pass in the tile; `masked`: some pair of
-  // the tile needs the index mask.
+  // is computed; the loop is unrolled by two so each step names its LDS buffers statically.
+  // `active`: this wave has pairs of the pass in the tile; `masked`: some pair of the tile
+  // needs the index mask.
   auto run_pass = [&](int kt_first, int n, const u32x4 (&qa)[NC], const uint16_t* ksrc, bool rotate_k,
                       bool local_pass, int lo_rel) __attribute__((always_inline)) {
     auto j0_of = [&](int t) { return (kt_first - t) * kBN; };
     u32x4 flo, fhi;
     if (rotate_k) {
       fetch_k(j0_of(0), flo, fhi);
-      commit_k(j0_of(0), s_k[0], flo, fhi);
+      commit_k(j0_of(0), s_k0, flo, fhi);
     } else {
-      stage_direct(ksrc, s_k[0], j0_of(0));
+      stage_direct(ksrc, s_k0, j0_of(0));
     }
-    stage_direct(vbase, s_v[0], j0_of(0));
+    stage_direct(vbase, s_v0, j0_of(0));
     wait_loads();
     __syncthreads();
-    for (int t = 0; t < n; ++t) {
-      const int buf = t & 1;
+    auto step = [&](int t, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
       const bool more = t + 1 < n;
       if (more) {
         if (rotate_k) fetch_k(j0_of(t + 1), flo, fhi);
-        else stage_direct(ksrc, s_k[buf ^ 1], j0_of(t + 1));
-        stage_direct(vbase, s_v[buf ^ 1], j0_of(t + 1));
+        else stage_direct(ksrc, kn, j0_of(t + 1));
+        stage_direct(vbase, vn, j0_of(t + 1));
       }
       const int j0 = j0_of(t);
       const int w_max = iw_last - j0, w_min = iw - (j0 + kBN - 1);
       const bool active = wave_live && (local_pass ? (w_max >= 0 && w_min < w0) : (w_max >= w0));
       if (active) {
         const bool masked = local_pass ? !(w_min >= 0 && w_max < w0) : (w_min < w0);
-        if (masked) tile_step(s_k[buf], s_v[buf], qa, j0, true, lo_rel, local_pass);
-        else tile_step(s_k[buf], s_v[buf], qa, j0, false, lo_rel, local_pass);
+        if (masked) tile_step(kc, vc, qa, j0, true, lo_rel, local_pass);
+        else tile_step(kc, vc, qa, j0, false, lo_rel, local_pass);
       }
-      if (more && rotate_k) commit_k(j0_of(t + 1), s_k[buf ^ 1], flo, fhi);
+      if (more && rotate_k) commit_k(j0_of(t + 1), kn, flo, fhi);
       wait_loads();
       __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < n; t += 2) {
+      step(t, s_k0, s_v0, s_k1, s_v1);
+      step(t + 1, s_k1, s_v1, s_k0, s_v0);
     }
+    if (t < n) step(t, s_k0, s_v0, s_k1, s_v1);
   };
 
   // ---------------- pass A: local pairs, tiles n_kt-1 down to kt_lo ----------------
