@@ -1,19 +1,13 @@
-// decode.hip -- single-token Dynamic Bifocal RoPE decode for gfx950: split-K + LSE reduce.
-//
-// The new token's query sits at position p = L - 1 and attends keys 0..L-1 of a cache that
-// holds keys rotated at their BASE absolute positions. G is recomputed from this step's L.
-// Keys with p - j < w0 (the last w0 keys) are local and use the base score q~ . k~_j; older
-// keys are remote and are moved to aliased positions by the correction rotation
-// R(Delta_j) k~_j, built in registers from the cached base key, so the cache is never
-// rewritten when G changes (review page, Method; gist.science summary, Methodologie
-// section 2: correction rotation of the active query and cached keys, additive composition).
-//
-// Split kernel: one wave per (key chunk, KV head, batch). The wave streams 32-key blocks:
-//   K rows load straight into MFMA A-operand registers (lane = key), are rotated in
-//   registers, and S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16 with the KV head's query
-//   heads as columns; V is transposed through a small LDS tile for O^T = V^T P^T.
-//   Local and remote contributions share one running max; the wave writes the partial
-//   (max, sum, unnormalised output) of its chunk to the workspace.
+// Split kernel: one workgroup of 8 waves per (key chunk, group of 8 KV heads, batch); wave w
+//   owns KV head 8*blockIdx.y + w and walks the chunk in 32-key blocks. The 8 waves read the
+//   same keys, so the workgroup streams each position's contiguous 2 KB of K and of V.
+//   K rows load straight into MFMA A-operand registers (lane = key) and are rotated in
+//   registers; V goes global->LDS by direct loads into a per-wave swizzled tile and is read
+//   back transposed for O^T = V^T P^T. Each wave keeps the next block's K and V loads in
+//   flight while it computes the current block (decode is a pure HBM stream; this keeps
+//   ~128 KB per CU outstanding). S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16 with the KV
+//   head's query heads as columns. Local and remote contributions share one running max; the
+//   wave writes the partial (max, sum, unnormalised output) of its chunk to the workspace.
 // Reduce kernel: merges the partials of all chunks by log-sum-exp and writes bf16 o / lse.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -33,36 +27,50 @@ struct DecodeArgs {
   uint32_t W[D / 2];
 };
 
-template <int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs<D> a) {
-  constexpr int NC = D / 16;
-  constexpr int NDB = D / 32;
-  constexpr int VP = 32 + 4;  // V^T pitch (bf16) for a 32-key block: 2 banks mod 32 per row
-  __shared__ __align__(16) uint16_t s_vt[D * VP];
-  __shared__ uint32_t s_w[D / 2];
+constexpr int kDecWaves = 8;
+constexpr int kDecBlock = 32;  // keys per block
 
-  const int lane = threadIdx.x, h = lane >> 5, col = lane & 31;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+template <int D>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_split_kernel(const DecodeArgs<D> a) {
+  constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8, RPI = 64 / CPR;
+  constexpr int VSZ = kDecBlock * D;       // elements of one wave's V tile
+  constexpr int NLD = kDecBlock / RPI;     // direct loads per V tile
+  // Separate objects per buffer so reads of one do not wait for direct loads into the other.
+  __shared__ __align__(16) uint16_t s_v0[kDecWaves * VSZ], s_v1[kDecWaves * VSZ];
+  __shared__ __align__(16) uint32_t s_w[D / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int split = blockIdx.x, b = blockIdx.z;
+  const int g = blockIdx.y * kDecWaves + wave;  // KV head of this wave
   const int Hg = a.Hq / a.Hkv;
   const int L = a.L, p = L - 1, w0 = a.w0, G = a.G;
 
-  for (int t = lane; t < D / 2; t += 64) s_w[t] = a.W[t];
-  __syncthreads();
+  for (int t = tid; t < D / 2; t += 64 * kDecWaves) s_w[t] = a.W[t];
+  __syncthreads();  // the only workgroup barrier: waves are independent from here on
+  if (g >= a.Hkv) return;
 
-  // Query operands (B of S^T = K Q^T): column col = query head g*Hg + col (zero if col >= Hg).
-  u32x4 qt[NC], qr[NC];
-  {
-    const uint16_t* src = a.q + ((size_t)b * a.Hq + (size_t)g * Hg + col) * D + 8 * h;
+  // Query operands (B of S^T = K Q^T): column col = query head g*Hg + col (zero if col >= Hg),
+  // scaled into log2 units. qr = R(Delta_p) q~ stays in registers; q~ itself is only needed for
+  // the blocks holding the last w0 keys and is re-read there.
+  const uint16_t* qsrc = a.q + ((size_t)b * a.Hq + (size_t)g * Hg + col) * D + 8 * h;
+  auto load_q = [&](u32x4 (&raw)[NC]) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      qt[c] = u32x4{0, 0, 0, 0};
-      if (col < Hg) qt[c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+      raw[c] = u32x4{0, 0, 0, 0};
+      if (col < Hg) raw[c] = *reinterpret_cast<const u32x4*>(qsrc + 16 * c);
     }
+  };
+  u32x4 qr[NC];
+  {
+    u32x4 raw[NC];
+    load_q(raw);
     const int dq = correction_offset(p, G);
 #pragma unroll
     for (int c = 0; c < NC / 2; ++c) {
-      u32x4 lo = qt[c], hi = qt[c + NC / 2];
-      rotate8(lo, hi, dq, &s_w[16 * c + 8 * h]);
+      u32x4 lo = raw[c], hi = raw[c + NC / 2];
+      rotate8_scaled(lo, hi, dq, &s_w[16 * c + 8 * h], a.scale_log2);
       qr[c] = lo;
       qr[c + NC / 2] = hi;
     }
@@ -73,120 +81,136 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs<D> a)
   const uint16_t* vbase = a.vc + (size_t)b * a.cap * row_stride + (size_t)g * D;
   const int k_begin = split * a.chunk;
   const int k_end = min(L, k_begin + a.chunk);
+  const int nblk = (k_end - k_begin + kDecBlock - 1) / kDecBlock;
+  uint16_t* vb0 = s_v0 + wave * VSZ;
+  uint16_t* vb1 = s_v1 + wave * VSZ;
+
+  // K block: lane (col, h) holds key blk+col, d = 16c + 8h .. +8 (rows past L clamped to L-1;
+  // their scores are masked).
+  auto load_k = [&](int blk, u32x4 (&kr)[NC]) __attribute__((always_inline)) {
+    const int j = min(blk + col, L - 1);
+    const uint16_t* src = kbase + (size_t)j * row_stride + 8 * h;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+  };
+  // V block -> this wave's LDS tile: load n fills rows RPI*n + lane/CPR, slot lane%CPR holding
+  // global chunk slot ^ swz(row).
+  auto load_v = [&](int blk, uint16_t* vb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+      const int row = RPI * n + lane / CPR;
+      const int j = min(blk + row, L - 1);
+      load_lds16(vbase + (size_t)j * row_stride + 8 * ((lane % CPR) ^ swz<D>(row)), vb + RPI * n * D);
+    }
+  };
 
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
+  const int tr_r = lane & 15;
+  const int tr_key = 4 * h + (tr_r >> 2);
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_r & 3);
 
-  for (int blk = k_begin; blk < k_end; blk += 32) {
-    // ---- K block: lane (col, h) holds key blk+col, d = 16c + 8h .. +8 ----
-    const int j = blk + col;
-    u32x4 kreg[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kreg[c] = u32x4{0, 0, 0, 0};
-      if (j < L) kreg[c] = *reinterpret_cast<const u32x4*>(kbase + (size_t)j * row_stride + 16 * c + 8 * h);
-    }
-    // ---- V block -> LDS transposed (units of 4 keys x 8 d) ----
-#pragma unroll
-    for (int rep = 0; rep < (8 * (D / 8)) / 64; ++rep) {
-      const int u = lane + 64 * rep;
-      const int kg = u / (D / 8), dg = u % (D / 8);
-      u32x4 row[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int jj = blk + 4 * kg + r;
-        row[r] = u32x4{0, 0, 0, 0};
-        if (jj < L) row[r] = *reinterpret_cast<const u32x4*>(vbase + (size_t)jj * row_stride + 8 * dg);
-      }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1;
-        u32x2 out;
-        if ((dd & 1) == 0) {
-          out[0] = (row[0][w] & 0xffffu) | (row[1][w] << 16);
-          out[1] = (row[2][w] & 0xffffu) | (row[3][w] << 16);
-        } else {
-          out[0] = (row[0][w] >> 16) | (row[1][w] & 0xffff0000u);
-          out[1] = (row[2][w] >> 16) | (row[3][w] & 0xffff0000u);
-        }
-        *reinterpret_cast<u32x2*>(s_vt + (8 * dg + dd) * VP + 4 * kg) = out;
-      }
-    }
-
-    // ---- scores ----
-    const bool has_loc = (w0 > 0) && (p - (blk + 31) < w0);
+  // `after_scores` runs once the K registers have been consumed (it reloads them for the
+  // next block, so the K loads overlap this block's softmax and PV).
+  auto compute = [&](int blk, u32x4 (&kr)[NC], const uint16_t* vb, auto after_scores) __attribute__((always_inline)) {
+    // Keys blk .. blk+31: local iff p - j < w0 (the last w0 keys), else remote.
+    const bool has_loc = (w0 > 0) && (p - (blk + kDecBlock - 1) < w0);
     const bool has_rem = (p - blk) >= w0;
     f32x16 s = f32x16{};
-    if (has_rem) {
-      u32x4 kr[NC];
-      const int dk = correction_offset(j < L ? j : 0, G);
-#pragma unroll
-      for (int c = 0; c < NC / 2; ++c) {
-        u32x4 lo = kreg[c], hi = kreg[c + NC / 2];
-        rotate8(lo, hi, dk, &s_w[16 * c + 8 * h]);
-        kr[c] = lo;
-        kr[c + NC / 2] = hi;
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) s = mfma32(kr[c], qr[c], s);
-    }
     if (has_loc) {
+      u32x4 qt[NC];
+      load_q(qt);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) s = mfma32(kr[c], scale8(qt[c], a.scale_log2), s);
+    }
+    if (has_rem) {
+      // Correction rotation R(Delta_j) of this lane's key, in place.
+      const int dk = correction_offset(min(blk + col, L - 1), G);
+#pragma unroll
+      for (int c = 0; c < NC / 2; ++c) rotate8(kr[c], kr[c + NC / 2], dk, &s_w[16 * c + 8 * h]);
       f32x16 t = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) t = mfma32(kreg[c], qt[c], t);
-      if (has_rem) {
+      for (int c = 0; c < NC; ++c) t = mfma32(kr[c], qr[c], t);
+      if (has_loc) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (p - (blk + c_row(r, h)) < w0) s[r] = t[r];
+          if (p - (blk + c_row(r, h)) >= w0) s[r] = t[r];
       } else {
         s = t;
       }
     }
-
-    // ---- online softmax for this lane's column (query head) ----
-    const bool tail = blk + 31 >= L;
+    after_scores();
+    if (blk + kDecBlock > L) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (blk + c_row(r, h) >= L) s[r] = kNegBig;
+    }
+    // Online softmax for this lane's column (query head), lazily raised max.
     float mx = kNegBig;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[r] * a.scale_log2;
-      if (tail && blk + c_row(r, h) >= L) x = kNegBig;
-      s[r] = x;
-      mx = fmaxf(mx, x);
-    }
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[r], s[r + 1]));
     mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    const bool up = mx > m_run + 8.0f;
+    if (wave_any(up)) {
+      const float m_new = up ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-    float ps = 0.f;
-    u32x4 pb[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = fast_exp2(s[r] - m_new);
-      ps += s[r];
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
+    u32x4 pb[2];
+    float ps = 0.f;
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) pb[ch][w] = pack_bf16x2(s[8 * ch + 2 * w], s[8 * ch + 2 * w + 1]);
+      for (int w = 0; w < 4; ++w) {
+        const int r = 8 * ch + 2 * w;
+        const uint32_t pk = pack_bf16x2(fast_exp2(s[r] - m_run), fast_exp2(s[r + 1] - m_run));
+        pb[ch][w] = pk;
+        ps = sum_bf16x2(pk, ps);
+      }
     l_run += ps;
-
-    __syncthreads();  // V^T tile written
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int ch = 0; ch < 2; ++ch) {
+      const int key0 = 16 * ch + tr_key, key1 = key0 + 8;
+      const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        const uint16_t* vr = s_vt + (32 * db + col) * VP + 16 * ch + 4 * h;
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 8);
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + tr_d;
+        const u32x2 v0 = read_tr(vb + key0 * D + 8 * ((d >> 3) ^ sw0) + (d & 7));
+        const u32x2 v1 = read_tr(vb + key1 * D + 8 * ((d >> 3) ^ sw1) + (d & 7));
         o[db] = mfma32(u32x4{v0[0], v0[1], v1[0], v1[1]}, pb[ch], o[db]);
       }
-    __syncthreads();  // before the next block overwrites the tile
+    }
+  };
+
+  // Block i: its V tile was requested one block earlier (direct loads, double-buffered LDS); its
+  // K registers were reloaded right after block i-1's score MFMAs.
+  u32x4 kr[NC];
+  load_k(k_begin, kr);
+  load_v(k_begin, vb0);
+  auto step = [&](int i, const uint16_t* vc, uint16_t* vn) __attribute__((always_inline)) {
+    const int blk = k_begin + i * kDecBlock;
+    const bool more = i + 1 < nblk;
+    if (more) {
+      load_v(blk + kDecBlock, vn);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");  // block i's K and V are in
+    } else {
+      wait_loads();
+    }
+    compute(blk, kr, vc, [&]() {
+      if (more) load_k(blk + kDecBlock, kr);
+    });
+  };
+  int i = 0;
+  for (; i + 1 < nblk; i += 2) {
+    step(i, vb0, vb1);
+    step(i + 1, vb1, vb0);
   }
+  if (i < nblk) step(i, vb0, vb1);
 
   const float l_tot = pair_sum(l_run);
   if (col < Hg) {
@@ -257,8 +281,9 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
 }
 
 DecodeSplit decode_split(long long L, int batch, int n_kv_heads) {
-  // Aim for ~2048 waves in flight-sized grids (8 per CU on 256 CUs), 32-key granularity.
-  const long long target = (2048 + (long long)batch * n_kv_heads - 1) / ((long long)batch * n_kv_heads);
+  // One 8-wave workgroup per CU (its V tiles use 128 KB of LDS): aim for 256 workgroups.
+  const long long groups = (long long)batch * ((n_kv_heads + kDecWaves - 1) / kDecWaves);
+  const long long target = (256 + groups - 1) / groups;
   const long long blocks = (L + 31) / 32;
   long long ns = blocks < target ? blocks : target;
   if (ns < 1) ns = 1;
@@ -286,7 +311,8 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
   a.chunk = p.chunk;
   a.scale_log2 = p.scale_log2;
   for (int i = 0; i < D / 2; ++i) a.W[i] = p.W[i];
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(p.n_splits, p.n_kv_heads, p.batch), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(p.n_splits, (p.n_kv_heads + kDecWaves - 1) / kDecWaves, p.batch),
+                     dim3(64 * kDecWaves), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, p.batch), dim3(256), 0, stream,

@@ -79,34 +79,6 @@ struct Tile {
   static constexpr int TSZ = kBN * D;      // elements per tile (rows are unpadded)
 };
 
-// Key/value tiles are row-major with 16-byte chunk c of row r stored at position c ^ swz(r).
-// LDS has 64 four-byte banks, i.e. one 256-byte line. D = 128 (one row per line): swz(r) is a
-// 4-bit permutation of r mod 16, so 16 consecutive rows read at one chunk (the K operand,
-// ds_read_b128, 16 lanes per cycle) hit 16 distinct bank groups, and 4 consecutive rows read
-// at chunks 0..3 (the transposed V operand, ds_read_b64_tr_b16, 32 lanes per cycle) hit
-// disjoint groups. D = 64 (two rows per line): the same two properties per row parity.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-#define LDS_AS __attribute__((address_space(3)))
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane.
-__device__ __forceinline__ void load_lds16(const void* g, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Transposed read: within each 16-lane group, lane r names 4 consecutive bf16 of row r of a
-// 16x4 block M; lane i receives M[4e + i/4][i%4] for e = 0..3.
-__device__ __forceinline__ u32x2 read_tr(const uint16_t* lds) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(lds));
-  return __builtin_bit_cast(u32x2, r);
-}
-
 __device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
 
 // Kernel variants: every pair local (plain causal RoPE attention: w0 >= L or G = 1), or
