@@ -246,37 +246,67 @@ __device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) 
   return r;
 }
 
+// Reduce: one workgroup of 256 threads per (query head, 32-wide slice of d, batch). Thread t
+// owns splits t, t+256, ...; all of its partial loads are issued up front, then the block max of
+// the split maxima, the weights exp2(m_s - M), and the weighted sums of 32 outputs are reduced
+// across the 4 waves through LDS.
+constexpr int kRedThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
-                                                            float* __restrict__ lse, int Hq, int n_splits) {
-  constexpr int P = 256 / D;
-  __shared__ float s_wt[kMaxSplits];
-  __shared__ float s_red[4];
-  __shared__ float s_acc[256];
-  const int head = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+__global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
+                                                                    float* __restrict__ lse, int Hq, int n_splits) {
+  __shared__ float s_red[kRedThreads / 64];
+  __shared__ float s_acc[kRedThreads / 64][33];
+  const int head = blockIdx.x, slice = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const float* src = ws + ((size_t)b * Hq + head) * n_splits * (D + 2);
+  // Pass 1: maxima of this thread's splits.
   float m = kNegBig;
-  for (int s = t; s < n_splits; s += 256) m = fmaxf(m, src[(size_t)s * (D + 2)]);
-  const float M = block_reduce(m, s_red, true);
-  float den = 0.f;
-  for (int s = t; s < n_splits; s += 256) {
-    const float w = fast_exp2(src[(size_t)s * (D + 2)] - M);
-    s_wt[s] = w;
-    den += w * src[(size_t)s * (D + 2) + 1];
-  }
-  den = block_reduce(den, s_red, false);  // ends with a barrier: s_wt is complete
-  const int d = t % D, part = t / D;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int s = part; s < n_splits; s += P) acc += s_wt[s] * src[(size_t)s * (D + 2) + 2 + d];
-  s_acc[t] = acc;
-  __syncthreads();
-  if (t < D) {
-    float tot = 0.f;
+  for (int s = t; s < n_splits; s += kRedThreads) m = fmaxf(m, src[(size_t)s * (D + 2)]);
 #pragma unroll
-    for (int q = 0; q < P; ++q) tot += s_acc[q * D + t];
-    o[((size_t)b * Hq + head) * D + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(tot / den));
-    if (lse != nullptr && t == 0) lse[(size_t)b * Hq + head] = (M + __log2f(den)) * 0.69314718055994531f;
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  float M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kRedThreads / 64; ++w) M = fmaxf(M, s_red[w]);
+  // Pass 2: weighted sums of the denominators and of this slice's 32 outputs.
+  float den = 0.f, acc[32];
+#pragma unroll
+  for (int d = 0; d < 32; ++d) acc[d] = 0.f;
+  for (int s = t; s < n_splits; s += kRedThreads) {
+    const float* ps = src + (size_t)s * (D + 2);
+    const float w = fast_exp2(ps[0] - M);
+    den += w * ps[1];
+    const f32x4* pv = reinterpret_cast<const f32x4*>(ps + 2 + 32 * slice);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 v = pv[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * q + e] += w * v[e];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    den += __shfl_xor(den, off);
+#pragma unroll
+    for (int d = 0; d < 32; ++d) acc[d] += __shfl_xor(acc[d], off);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int d = 0; d < 32; ++d) s_acc[wave][d] = acc[d];
+    s_acc[wave][32] = den;
+  }
+  __syncthreads();
+  if (t < 32) {
+    float tot = 0.f, dtot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRedThreads / 64; ++w) {
+      tot += s_acc[w][t];
+      dtot += s_acc[w][32];
+    }
+    o[((size_t)b * Hq + head) * D + 32 * slice + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(tot / dtot));
+    if (lse != nullptr && slice == 0 && t == 0) lse[(size_t)b * Hq + head] = (M + __log2f(dtot)) * 0.69314718055994531f;
   }
 }
 
@@ -315,7 +345,7 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
                      dim3(64 * kDecWaves), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, p.batch), dim3(256), 0, stream,
+  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, D / 32, p.batch), dim3(kRedThreads), 0, stream,
                      (const float*)p.workspace, static_cast<uint16_t*>(p.o), p.lse, p.n_q_heads, p.n_splits);
   return hipGetLastError();
 }
