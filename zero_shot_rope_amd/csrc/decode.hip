@@ -1,14 +1,18 @@
 // Split kernel: one workgroup of 8 waves per (key chunk, group of 8 KV heads, batch); wave w
 //   owns KV head 8*blockIdx.y + w and walks the chunk in 32-key blocks. The 8 waves read the
 //   same keys, so the workgroup streams each position's contiguous 2 KB of K and of V.
-//   K rows load straight into MFMA A-operand registers (lane = key) and are rotated in
-//   registers; V goes global->LDS by direct loads into a per-wave swizzled tile and is read
-//   back transposed for O^T = V^T P^T. Each wave keeps the next block's K and V loads in
-//   flight while it computes the current block (decode is a pure HBM stream; this keeps
-//   ~128 KB per CU outstanding). S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16 with the KV
-//   head's query heads as columns. Local and remote contributions share one running max; the
-//   wave writes the partial (max, sum, unnormalised output) of its chunk to the workspace.
+//   The correction angles depend only on the key position, so the workgroup computes one
+//   cos/sin table per block (32 keys x D/2 frequencies) into LDS and every head's wave rotates
+//   its keys with it. Score and output products run on v_mfma_f32_16x16x32_bf16: a KV head has
+//   at most 4 query heads, so 16 output columns waste less than 32 and halve the accumulator.
+//   K rows load straight into A-operand registers (two register sets, so the next block's keys
+//   are in flight for a whole block); V goes global->LDS by direct loads into a per-wave
+//   double-buffered swizzled tile read back transposed for O^T = V^T P^T. Local and remote
+//   contributions share one running max; the wave writes the partial (max, sum, unnormalised
+//   output) of its chunk to the workspace.
 // Reduce kernel: merges the partials of all chunks by log-sum-exp and writes bf16 o / lse.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -28,129 +32,222 @@ struct DecodeArgs {
 };
 
 constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecBlock = 32;  // keys per block
 
+// V tiles: row-major 32 x D, 16-byte chunk c of row r stored at chunk c ^ vswz(r). A transposed
+// read covers 16 rows x 32 bytes (two adjacent chunks 2m, 2m+1) per wave, 8 rows per half-wave:
+// vswz permutes the chunk pairs so 8 consecutive rows land in 8 distinct 32-byte bank groups
+// (D = 128: one row per 256-byte bank line; D = 64: two rows per line, split by row parity).
 template <int D>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__device__ __forceinline__ int vswz(int row) {
+  if constexpr (D == 128) return 2 * (row & 7);
+  else return 2 * ((row >> 1) & 3);
+}
+
+// Workgroup barrier for the ds_write -> ds_read hand-over of the angle tables: waits for this
+// wave's LDS operations only. __syncthreads (and a workgroup fence on LDS) would also wait for
+// the direct global->LDS loads kept in flight across it. The memory clobber keeps the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt with only the vector-memory counter set (gfx9 encoding: vmcnt bits [3:0] and
+// [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their no-wait maxima). As a builtin, unlike
+// inline asm, the compiler's own wait-count tracking sees it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(const DecodeArgs<D> a) {
-  constexpr int NC = D / 16, NDB = D / 32, CPR = D / 8, RPI = 64 / CPR;
+  constexpr int HALF = D / 2;
+  constexpr int NQC = D / 32;              // 32-wide d chunks of the score contraction
+  constexpr int NKR = 2 * NQC;             // K registers (u32x4) per block: 2 key groups
+  constexpr int NOB = D / 16;              // 16-row d blocks of O^T
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
   constexpr int VSZ = kDecBlock * D;       // elements of one wave's V tile
   constexpr int NLD = kDecBlock / RPI;     // direct loads per V tile
+  constexpr int TSZ = kDecBlock * D;       // floats of one angle table: per key D/2 (cos, sin)
+  constexpr int TPT = kDecBlock * HALF / kDecThreads;  // table entries per thread
   // Separate objects per buffer so reads of one do not wait for direct loads into the other.
   __shared__ __align__(16) uint16_t s_v0[kDecWaves * VSZ], s_v1[kDecWaves * VSZ];
-  __shared__ __align__(16) uint32_t s_w[D / 2];
+  __shared__ __align__(16) float s_t0[TSZ], s_t1[TSZ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, col = lane & 31;
+  const int li = lane & 15, lg = lane >> 4;  // MFMA 16x16 lane = li + 16 * lg
   const int split = blockIdx.x, b = blockIdx.z;
   const int g = blockIdx.y * kDecWaves + wave;  // KV head of this wave
+  const bool head_live = g < a.Hkv;
+  const int gl = head_live ? g : 0;
   const int Hg = a.Hq / a.Hkv;
   const int L = a.L, p = L - 1, w0 = a.w0, G = a.G;
 
-  for (int t = tid; t < D / 2; t += 64 * kDecWaves) s_w[t] = a.W[t];
-  __syncthreads();  // the only workgroup barrier: waves are independent from here on
-  if (g >= a.Hkv) return;
-
-  // Query operands (B of S^T = K Q^T): column col = query head g*Hg + col (zero if col >= Hg),
-  // scaled into log2 units. qr = R(Delta_p) q~ stays in registers; q~ itself is only needed for
-  // the blocks holding the last w0 keys and is re-read there.
-  const uint16_t* qsrc = a.q + ((size_t)b * a.Hq + (size_t)g * Hg + col) * D + 8 * h;
-  auto load_q = [&](u32x4 (&raw)[NC]) __attribute__((always_inline)) {
+  // Query operands (B of S^T = K Q^T): column li = query head g*Hg + li (zero if li >= Hg), rows
+  // d = 32c + 8lg .. +8, scaled into log2 units: qs = q~ for local keys, qr = R(Delta_p) q~ for
+  // remote keys. Both stay in registers for the whole chunk.
+  const bool q_live = head_live && li < Hg;
+  const uint16_t* qsrc = a.q + ((size_t)b * a.Hq + (size_t)gl * Hg + (q_live ? li : 0)) * D + 8 * lg;
+  auto load_q = [&](u32x4 (&raw)[NQC]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      raw[c] = u32x4{0, 0, 0, 0};
-      if (col < Hg) raw[c] = *reinterpret_cast<const u32x4*>(qsrc + 16 * c);
-    }
+    for (int c = 0; c < NQC; ++c) raw[c] = *reinterpret_cast<const u32x4*>(qsrc + 32 * c);
   };
-  u32x4 qr[NC];
+  auto mask_q = [&](u32x4 (&raw)[NQC]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < NQC; ++c)
+      if (!q_live) raw[c] = u32x4{0, 0, 0, 0};
+  };
+  u32x4 qr[NQC], qs[NQC];
   {
-    u32x4 raw[NC];
+    u32x4 raw[NQC];
     load_q(raw);
+    mask_q(raw);
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) qs[c] = scale8(raw[c], a.scale_log2);
     const int dq = correction_offset(p, G);
 #pragma unroll
-    for (int c = 0; c < NC / 2; ++c) {
-      u32x4 lo = raw[c], hi = raw[c + NC / 2];
-      rotate8_scaled(lo, hi, dq, &s_w[16 * c + 8 * h], a.scale_log2);
+    for (int c = 0; c < NQC / 2; ++c) {
+      u32x4 lo = raw[c], hi = raw[c + NQC / 2];
+      rotate8_scaled(lo, hi, dq, &a.W[32 * c + 8 * lg], a.scale_log2);
       qr[c] = lo;
-      qr[c + NC / 2] = hi;
+      qr[c + NQC / 2] = hi;
     }
   }
 
   const size_t row_stride = (size_t)a.Hkv * D;
-  const uint16_t* kbase = a.kc + (size_t)b * a.cap * row_stride + (size_t)g * D;
-  const uint16_t* vbase = a.vc + (size_t)b * a.cap * row_stride + (size_t)g * D;
+  const uint16_t* kbase = a.kc + (size_t)b * a.cap * row_stride + (size_t)gl * D;
+  const uint16_t* vbase = a.vc + (size_t)b * a.cap * row_stride + (size_t)gl * D;
   const int k_begin = split * a.chunk;
   const int k_end = min(L, k_begin + a.chunk);
   const int nblk = (k_end - k_begin + kDecBlock - 1) / kDecBlock;
-  uint16_t* vb0 = s_v0 + wave * VSZ;
-  uint16_t* vb1 = s_v1 + wave * VSZ;
+  // LDS buffers are named statically (buffer 0/1 of V and of the angle table) and indexed with
+  // one integer offset, so the compiler can tell every LDS read from the direct loads in flight
+  // into the other buffer.
+  auto vtile = [&](auto buf) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(buf)::value == 0) return s_v0;
+    else return s_v1;
+  };
+  auto table = [&](auto buf) __attribute__((always_inline)) -> float* {
+    if constexpr (decltype(buf)::value == 0) return s_t0;
+    else return s_t1;
+  };
+  const int vwave = wave * VSZ;
 
-  // K block: lane (col, h) holds key blk+col, d = 16c + 8h .. +8 (rows past L clamped to L-1;
-  // their scores are masked).
-  auto load_k = [&](int blk, u32x4 (&kr)[NC]) __attribute__((always_inline)) {
-    const int j = min(blk + col, L - 1);
-    const uint16_t* src = kbase + (size_t)j * row_stride + 8 * h;
+  // K block: lane (li, lg) holds keys blk + li (registers 0..NQC-1) and blk + 16 + li
+  // (NQC..2NQC-1), d = 32c + 8lg .. +8. Rows past L are clamped to L-1; their scores are masked.
+  auto load_k = [&](int blk, u32x4 (&kr)[NKR]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = *reinterpret_cast<const u32x4*>(src + 16 * c);
+    for (int kg = 0; kg < 2; ++kg) {
+      const int j = min(blk + 16 * kg + li, L - 1);
+      const uint16_t* src = kbase + (size_t)j * row_stride + 8 * lg;
+#pragma unroll
+      for (int c = 0; c < NQC; ++c) kr[kg * NQC + c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+    }
   };
   // V block -> this wave's LDS tile: load n fills rows RPI*n + lane/CPR, slot lane%CPR holding
-  // global chunk slot ^ swz(row).
-  auto load_v = [&](int blk, uint16_t* vb) __attribute__((always_inline)) {
+  // global chunk slot ^ vswz(row).
+  auto load_v = [&](int blk, auto buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
       const int row = RPI * n + lane / CPR;
       const int j = min(blk + row, L - 1);
-      load_lds16(vbase + (size_t)j * row_stride + 8 * ((lane % CPR) ^ swz<D>(row)), vb + RPI * n * D);
+      load_lds16(vbase + (size_t)j * row_stride + 8 * ((lane % CPR) ^ vswz<D>(row)),
+                 vtile(buf) + (vwave + RPI * n * D));
     }
   };
-
-  f32x16 o[NDB];
+  // Angle table of a block: row = key, (cos, sin) of Delta_j * omega_k at floats 2k, 2k+1, with
+  // 16-byte chunk c of row r stored at chunk c ^ (r & 15) (16 rows read at one chunk hit 16
+  // distinct bank groups). Thread t fills frequency t % HALF of keys t / HALF + (threads/HALF) n.
+  const int t_k = tid % HALF, t_key0 = tid / HALF;
+  const uint32_t t_w = a.W[t_k];
+  auto fill_table = [&](int blk, auto buf) __attribute__((always_inline)) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  float m_run = kNegBig, l_run = 0.f;
-  const int tr_r = lane & 15;
-  const int tr_key = 4 * h + (tr_r >> 2);
-  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_r & 3);
+    for (int n = 0; n < TPT; ++n) {
+      const int key = t_key0 + (kDecThreads / HALF) * n;
+      float sn, cs;
+      turns_sincos(phase_turns(correction_offset(min(blk + key, L - 1), G), t_w), sn, cs);
+      *reinterpret_cast<f32x2*>(table(buf) + (key * D + 4 * ((t_k >> 1) ^ (key & 15)) + 2 * (t_k & 1))) =
+          f32x2{cs, sn};
+    }
+  };
+  const bool need_table = (p - k_begin) >= w0;  // some key of this chunk is remote
 
-  // `after_scores` runs once the K registers have been consumed (it reloads them for the
-  // next block, so the K loads overlap this block's softmax and PV).
-  auto compute = [&](int blk, u32x4 (&kr)[NC], const uint16_t* vb, auto after_scores) __attribute__((always_inline)) {
-    // Keys blk .. blk+31: local iff p - j < w0 (the last w0 keys), else remote.
+  f32x4 o[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) o[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, l_run = 0.f;
+
+  // V^T operand rows d = 16ob + li of O^T = V^T P^T: in each 16-lane group, lane r names
+  // V[key + r/4][16ob + 4(r%4) .. +4] and receives V[key + e][16ob + li], e = 0..3, for the
+  // group's keys 4lg .. 4lg+3 (first read) and 16 + 4lg .. (second read).
+  const int tr_k0 = 4 * lg + (li >> 2), tr_k1 = tr_k0 + 16;
+  const int tr_lo = 4 * (li & 3);  // d offset within the 16-row block
+  const int tr_base0 = vwave + tr_k0 * D + (tr_lo & 7), tr_base1 = vwave + tr_k1 * D + (tr_lo & 7);
+  const int tr_sw0 = vswz<D>(tr_k0), tr_sw1 = vswz<D>(tr_k1);
+
+  // Keys blk .. blk+31: local iff p - j < w0 (the last w0 keys), else remote. Score register r
+  // of key group kg holds key blk + 16kg + 4lg + r for query column li.
+  auto compute = [&](int blk, const u32x4 (&kr)[NKR], auto buf) __attribute__((always_inline)) {
     const bool has_loc = (w0 > 0) && (p - (blk + kDecBlock - 1) < w0);
     const bool has_rem = (p - blk) >= w0;
-    f32x16 s = f32x16{};
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     if (has_loc) {
-      u32x4 qt[NC];
-      load_q(qt);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) s = mfma32(kr[c], scale8(qt[c], a.scale_log2), s);
-    }
-    if (has_rem) {
-      // Correction rotation R(Delta_j) of this lane's key, in place.
-      const int dk = correction_offset(min(blk + col, L - 1), G);
-#pragma unroll
-      for (int c = 0; c < NC / 2; ++c) rotate8(kr[c], kr[c + NC / 2], dk, &s_w[16 * c + 8 * h]);
-      f32x16 t = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) t = mfma32(kr[c], qr[c], t);
-      if (has_loc) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (p - (blk + c_row(r, h)) >= w0) s[r] = t[r];
-      } else {
-        s = t;
+      for (int c = 0; c < NQC; ++c) {
+        s[0] = mfma16(kr[c], qs[c], s[0]);
+        s[1] = mfma16(kr[NQC + c], qs[c], s[1]);
       }
     }
-    after_scores();
-    if (blk + kDecBlock > L) {
+    if (has_rem) {
+      // Correction rotation R(Delta_j) of this lane's keys with the block's shared table, into
+      // temporaries that feed the MFMAs directly (the loaded K registers stay read-only, so the
+      // compiler never copies a register whose load may still be in flight).
+      const float* tb = table(buf);
+      f32x4 t[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (blk + c_row(r, h) >= L) s[r] = kNegBig;
+      for (int kg = 0; kg < 2; ++kg) {
+        const int row = 16 * kg + li;
+#pragma unroll
+        for (int c = 0; c < NQC / 2; ++c) {
+          const u32x4 lo = kr[kg * NQC + c], hi = kr[kg * NQC + c + NQC / 2];
+          u32x4 olo, ohi;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            // Frequencies 32c + 8lg + 2w, +1: table chunk 16c + 4lg + w holds (c0, s0, c1, s1).
+            const f32x4 tc = *reinterpret_cast<const f32x4*>(tb + (row * D + 4 * ((16 * c + 4 * lg + w) ^ li)));
+            const float x0 = bf16lo(lo[w]), x1 = bf16hi(lo[w]), y0 = bf16lo(hi[w]), y1 = bf16hi(hi[w]);
+            olo[w] = pack_bf16x2(x0 * tc[0] - y0 * tc[1], x1 * tc[2] - y1 * tc[3]);
+            ohi[w] = pack_bf16x2(x0 * tc[1] + y0 * tc[0], x1 * tc[3] + y1 * tc[2]);
+          }
+          t[kg] = mfma16(olo, qr[c], t[kg]);
+          t[kg] = mfma16(ohi, qr[c + NQC / 2], t[kg]);
+        }
+      }
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {
+        if (has_loc) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (p - (blk + 16 * kg + 4 * lg + r) >= w0) s[kg][r] = t[kg][r];
+        } else {
+          s[kg] = t[kg];
+        }
+      }
     }
-    // Online softmax for this lane's column (query head), lazily raised max.
-    float mx = kNegBig;
+    if (blk + kDecBlock > k_end) {
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[r], s[r + 1]));
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (blk + 16 * kg + 4 * lg + r >= k_end) s[kg][r] = kNegBig;
+    }
+    // Online softmax for query column li (its 32 scores sit on lanes li, li+16, li+32, li+48),
+    // lazily raised max.
+    float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(s[0][0], s[0][1]), __builtin_fmaxf(s[0][2], s[0][3])),
+                               __builtin_fmaxf(__builtin_fmaxf(s[1][0], s[1][1]), __builtin_fmaxf(s[1][2], s[1][3])));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
     mx = pair_max(mx);
     const bool up = mx > m_run + 8.0f;
     if (wave_any(up)) {
@@ -159,91 +256,87 @@ void decode_split_kernel(const DecodeArgs<D> a) {
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      for (int ob = 0; ob < NOB; ++ob) o[ob] *= alpha;
     }
-    u32x4 pb[2];
+    // P^T as the B operand: lane (li, lg) element e is key 4lg + e (e < 4) or 16 + 4lg + e - 4
+    // (e >= 4), exactly the keys of its score registers and of the V^T reads.
+    u32x4 pb;
     float ps = 0.f;
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int r = 8 * ch + 2 * w;
-        const uint32_t pk = pack_bf16x2(fast_exp2(s[r] - m_run), fast_exp2(s[r + 1] - m_run));
-        pb[ch][w] = pk;
-        ps = sum_bf16x2(pk, ps);
-      }
+    for (int w = 0; w < 4; ++w) {
+      const int kg = w >> 1, r = 2 * (w & 1);
+      const uint32_t pk = pack_bf16x2(fast_exp2(s[kg][r] - m_run), fast_exp2(s[kg][r + 1] - m_run));
+      pb[w] = pk;
+      ps = sum_bf16x2(pk, ps);
+    }
     l_run += ps;
+    const uint16_t* vt = vtile(buf);
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      const int key0 = 16 * ch + tr_key, key1 = key0 + 8;
-      const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + tr_d;
-        const u32x2 v0 = read_tr(vb + key0 * D + 8 * ((d >> 3) ^ sw0) + (d & 7));
-        const u32x2 v1 = read_tr(vb + key1 * D + 8 * ((d >> 3) ^ sw1) + (d & 7));
-        o[db] = mfma32(u32x4{v0[0], v0[1], v1[0], v1[1]}, pb[ch], o[db]);
-      }
+    for (int ob = 0; ob < NOB; ++ob) {
+      const int ch = 2 * ob + (tr_lo >> 3);
+      const u32x2 v0 = read_tr(vt + (tr_base0 + 8 * (ch ^ tr_sw0)));
+      const u32x2 v1 = read_tr(vt + (tr_base1 + 8 * (ch ^ tr_sw1)));
+      o[ob] = mfma16(u32x4{v0[0], v0[1], v1[0], v1[1]}, pb, o[ob]);
     }
   };
 
-  // Block i: its V tile was requested one block earlier (direct loads, double-buffered LDS); its
-  // K registers were reloaded right after block i-1's score MFMAs.
-  u32x4 kr[NC];
-  load_k(k_begin, kr);
-  load_v(k_begin, vb0);
-  auto step = [&](int i, const uint16_t* vc, uint16_t* vn) __attribute__((always_inline)) {
+  // Step i: block i's K/V loads were issued one step earlier and its angle table filled before
+  // the previous barrier. Issue block i+1's loads and fill its table (other buffers), wait for
+  // block i's data, compute, barrier (table i+1 complete; table i free for block i+2).
+  const std::integral_constant<int, 0> B0{};
+  const std::integral_constant<int, 1> B1{};
+  // Waves past the last KV head (n_kv_heads not a multiple of 8) run the same loads and math on
+  // head 0's rows and discard the result: every load is then unconditional, which keeps the
+  // compiler's wait counts exact.
+  u32x4 ka[NKR], kb[NKR];
+  load_v(k_begin, B0);
+  load_k(k_begin, ka);
+  if (need_table) fill_table(k_begin, B0);
+  lds_barrier();
+  // MORE: a block i+1 exists (always true except for the chunk's last block).
+  auto step = [&](int i, u32x4 (&kc)[NKR], u32x4 (&kn)[NKR], auto cur, auto nxt, auto more) __attribute__((always_inline)) {
     const int blk = k_begin + i * kDecBlock;
-    const bool more = i + 1 < nblk;
-    if (more) {
-      load_v(blk + kDecBlock, vn);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");  // block i's K and V are in
+    if constexpr (decltype(more)::value) {
+      load_v(blk + kDecBlock, nxt);
+      load_k(blk + kDecBlock, kn);
+      if (need_table) fill_table(blk + kDecBlock, nxt);
+      wait_vmcnt<NKR + NLD>();  // block i's K and V are in
     } else {
-      wait_loads();
+      wait_vmcnt<0>();
     }
-    compute(blk, kr, vc, [&]() {
-      if (more) load_k(blk + kDecBlock, kr);
-    });
+    compute(blk, kc, cur);
+    lds_barrier();
   };
+  const std::true_type more_yes{};
+  const std::false_type more_no{};
   int i = 0;
-  for (; i + 1 < nblk; i += 2) {
-    step(i, vb0, vb1);
-    step(i + 1, vb1, vb0);
+  for (; i + 2 < nblk; i += 2) {
+    step(i, ka, kb, B0, B1, more_yes);
+    step(i + 1, kb, ka, B1, B0, more_yes);
   }
-  if (i < nblk) step(i, vb0, vb1);
+  if (i + 1 < nblk) {
+    step(i, ka, kb, B0, B1, more_yes);
+    step(i + 1, kb, ka, B1, B0, more_no);
+  } else if (i < nblk) {
+    step(i, ka, kb, B0, B1, more_no);
+  }
 
-  const float l_tot = pair_sum(l_run);
-  if (col < Hg) {
-    const int head = g * Hg + col;
+  // Column totals: the 4 lanes of query column li each summed 8 of its keys.
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot = pair_sum(l_tot);
+  if (q_live) {
+    const int head = g * Hg + li;
     float* dst = a.ws + (((size_t)b * a.Hq + head) * a.n_splits + split) * (D + 2);
-    if (h == 0) {
+    if (lg == 0) {
       dst[0] = m_run;
       dst[1] = l_tot;
     }
+    // O^T rows d = 16ob + 4lg + r of column li.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[2 + 32 * db + c_row(r, h)] = o[db][r];
+      for (int r = 0; r < 4; ++r) dst[2 + 16 * ob + 4 * lg + r] = o[ob][r];
   }
-}
-
-// One workgroup of 256 threads per (query head, batch): block max of the split maxima, per-split
-// weights in LDS, then thread (part, d) accumulates splits part, part+P, ... for element d.
-constexpr int kMaxSplits = 4096;
-
-__device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float y = __shfl_xor(x, off);
-    x = is_max ? fmaxf(x, y) : x + y;
-  }
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  __syncthreads();
-  return r;
 }
 
 // Reduce: one workgroup of 256 threads per (query head, 32-wide slice of d, batch). Thread t
@@ -342,7 +435,7 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
   a.scale_log2 = p.scale_log2;
   for (int i = 0; i < D / 2; ++i) a.W[i] = p.W[i];
   hipLaunchKernelGGL(decode_split_kernel<D>, dim3(p.n_splits, (p.n_kv_heads + kDecWaves - 1) / kDecWaves, p.batch),
-                     dim3(64 * kDecWaves), 0, stream, a);
+                     dim3(kDecThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, D / 32, p.batch), dim3(kRedThreads), 0, stream,

@@ -128,6 +128,15 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// MFMA 16x16x32 bf16 -> f32. Operand/result lane layout (wave64):
+//   A[i][k]: lane i + 16*(k/8), element k%8      (k < 32)
+//   B[k][j]: lane j + 16*(k/8), element k%8
+//   C[i][j]: lane j + 16*(i/4), register i%4
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // Value of lane l^32 (the other half of the wave) for every lane, via v_permlane32_swap.
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
