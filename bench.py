@@ -12,6 +12,7 @@ flop count 4 * Hq * D * L(L+1)/2 (one score and one PV product per causal pair);
 decode KV-cache bandwidth (4096 * L bytes per step) is reported beside it.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --prefill-only | --decode-only [--copy-calibration]   (profiling runs)
 """
 from __future__ import annotations
 
@@ -39,7 +40,45 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time for the baseline sample")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode leg (profiling runs)")
+    ap.add_argument("--decode-only", action="store_true", help="skip the prefill legs (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the run, copy a 1 GiB buffer once (a plain copy kernel of known size, the "
+                         "reference that scales the HBM byte counters of a profiled run)")
     return ap.parse_args()
+
+
+# HBM traffic per launch from rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE,
+# each in its own pass), each counter scaled by what it reads for the 1 GiB plain copy of
+# --copy-calibration in the same run. Valid only while the kernel sources hash to `sources`;
+# otherwise the kernel changed since the counters were taken and the traffic is reported as null.
+MEASURED_TRAFFIC = {
+    # rotate_keys_kernel + prefill_kernel<128, prerotated> at the 128K Qwen3-8B shape.
+    "prefill": {"sources": "e59695726f6469d4", "fetch_bytes": 19965.0e6, "write_bytes": 1443.0e6},
+    # decode_split_kernel + decode_reduce_kernel, mean over the 512 steps (L 98001..98512).
+    "decode": {"sources": "16a0ba0dd7ed671f", "fetch_bytes": 407.10e6, "write_bytes": 4.33e6},
+}
+_KERNEL_SOURCES = {
+    "prefill": ["prefill.hip", "device_common.hpp", "launch.hpp", "api.cpp"],
+    "decode": ["decode.hip", "device_common.hpp", "launch.hpp", "api.cpp"],
+}
+
+
+def sources_digest(which):
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "zero_shot_rope_amd", "csrc")
+    for name in _KERNEL_SOURCES[which]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(which):
+    rec = MEASURED_TRAFFIC[which]
+    if rec["sources"] is None or rec["sources"] != sources_digest(which):
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def main():
@@ -60,13 +99,20 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     pcfg, dcfg = W.QWEN3_8B_128K, W.QWEN3_8B_DECODE
-    t0 = time.time()
-    pb = W.prefill_inputs(pcfg)
+    do_prefill, do_decode = not args.decode_only, not args.prefill_only
+    if not (do_prefill or do_decode):
+        sys.exit("--prefill-only and --decode-only exclude each other")
     to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-    q, k, v = to_dev(pb["q"]), to_dev(pb["k"]), to_dev(pb["v"])
-    o = torch.empty_like(q)
-    log(f"prefill inputs {tuple(q.shape)} ready in {time.time() - t0:.1f}s")
-    if not args.prefill_only:
+    pb = None
+    if do_prefill:
+        t0 = time.time()
+        pb = W.prefill_inputs(pcfg)
+        q, k, v = to_dev(pb["q"]), to_dev(pb["k"]), to_dev(pb["v"])
+        o = torch.empty_like(q)
+        log(f"prefill inputs {tuple(q.shape)} ready in {time.time() - t0:.1f}s")
+        pws_bytes = Z.bifocal_prefill_workspace_bytes(pcfg.batch, pcfg.n_kv_heads, pcfg.head_dim, pcfg.L)
+        pws = torch.empty(pws_bytes, dtype=torch.uint8, device=dev)
+    if do_decode:
         db = W.decode_inputs(dcfg)
         kc, vc, qs = to_dev(db["k_cache"]), to_dev(db["v_cache"]), to_dev(db["q_steps"])
         od = torch.empty((dcfg.batch, dcfg.n_q_heads, dcfg.head_dim), dtype=torch.bfloat16, device=dev)
@@ -75,8 +121,6 @@ def main():
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         log(f"decode cache {tuple(kc.shape)} ready")
     sptr = stream.cuda_stream
-    pws_bytes = Z.bifocal_prefill_workspace_bytes(pcfg.batch, pcfg.n_kv_heads, pcfg.head_dim, pcfg.L)
-    pws = torch.empty(pws_bytes, dtype=torch.uint8, device=dev)
 
     def prefill(w0, fused=False):
         # Default: keys rotated once into the workspace, then the attention kernel. fused=True:
@@ -93,9 +137,10 @@ def main():
 
     def step(ev):
         ev[0].record(stream)
-        prefill(pcfg.w0)
+        if do_prefill:
+            prefill(pcfg.w0)
         ev[1].record(stream)
-        if not args.prefill_only:
+        if do_decode:
             decode_steps()
         ev[2].record(stream)
 
@@ -117,11 +162,11 @@ def main():
 
     flops = pcfg.flops()
     pre_avg = float(np.mean(pre_ms))
-    tflops = flops / (pre_avg * 1e-3) / 1e12
+    tflops = flops / (pre_avg * 1e-3) / 1e12 if do_prefill else None
 
     # Per-step decode timing (events around each call) for the G = 3 and G = 4 halves.
     decode = None
-    if not args.prefill_only:
+    if do_decode:
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(dcfg.steps + 1)]
         ev[0].record(stream)
         for t in range(dcfg.steps):
@@ -146,8 +191,15 @@ def main():
             "GBps_min": round(float(gbps.min()), 1),
             "bytes_per_step": "4096 * L (K and V rows of 8 KV heads x 128 dims, bf16, read once)",
             "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                         "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic("decode"),
+                         "traffic_unit": "bytes per decode step (split + reduce kernels)"},
         }
+
+    if not do_prefill:
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+        print(json.dumps({"decode": decode}), flush=True)
+        return
 
     # Matched control: the same kernel with every pair local (plain causal RoPE attention).
     cev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -198,7 +250,8 @@ def main():
         },
         "prefill_ms": round(pre_avg, 3),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic("prefill"),
+                     "traffic_unit": "bytes per prefill call (rotate + attention kernels)",
                      "kernel": "prefill_kernel<128, prerotated> (+ rotate_keys_kernel)", "flops_per_launch": flops},
         "prefill_mode": "keys rotated once into a workspace, then the fused attention kernel",
         "single_launch_mode": {"what": "no workspace: key rotation per staged tile inside the attention kernel",
@@ -209,7 +262,19 @@ def main():
         "decode": decode,
         "cpu_baseline": cpu,
     }
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration(torch, dev):
+    """One plain device copy of 1 GiB (reads 2^30 bytes, writes 2^30 bytes)."""
+    x = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    y = x.clone()
+    torch.cuda.synchronize()
+    log(f"copy calibration: {x.numel() * x.element_size()} bytes copied")
+    del x, y
 
 
 def cpu_baseline(pb, pcfg, target_s):
