@@ -39,6 +39,8 @@
 //   (the output is rescaled then); otherwise exponents stay <= kSlack.
 //   Workgroup ids are remapped so that each of the 8 XCDs owns a contiguous range of
 //   (batch, head unit, query tile) work, longest causal rows first.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -65,7 +67,10 @@ struct PrefillArgs {
 constexpr int kBN = 64;         // keys per tile
 constexpr int kWaves = 8;       // waves per workgroup (two per SIMD)
 constexpr int kThreads = 64 * kWaves;
-constexpr float kSlack = 8.0f;  // log2 units a row max may run ahead of the stored max
+// log2 units by which a row's scores may exceed the stored max before it is raised: P <= 2^64,
+// row sums <= 2^81 over 2^17 keys, far inside fp32 and bf16 range, so after a row's first tile
+// the max (and the rescale of O) practically never moves.
+constexpr float kSlack = 64.0f;
 
 template <int D>
 struct Tile {
@@ -209,128 +214,238 @@ void prefill_kernel(const PrefillArgs<D> a) {
   const int tr_key = 4 * h + (tr_r >> 2);
   const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_r & 3);
 
-  // One tile: S^T = K Q^T, index mask (masked tiles only), online softmax in log2 units with a
-  // lazily raised max, O^T += V^T P^T. Kept pairs: lo_rel <= i - j (and i - j < w0 in pass A).
-  auto tile_step = [&](const uint16_t* ks, const uint16_t* vs, const u32x4 (&qa)[NC], int j0, bool masked,
-                       int lo_rel, bool local_pass) __attribute__((always_inline)) {
-    f32x16 s[2];
+  // Half-tile pieces (32 keys, kb = 0 or 1 of a 64-key tile). qk: S^T = K Q^T (8 MFMAs).
+  // mask: index mask of masked tiles (kept pairs: lo_rel <= i - j, and i - j < w0 in pass A).
+  // exps: P^T = exp2(S^T - m) in bf16 and the lane's row sum (VALU). pv: O^T += V^T P^T
+  // (8 MFMAs).
+  auto qk = [&](const uint16_t* ks, int kb, const u32x4 (&qa)[NC], f32x16& s) __attribute__((always_inline)) {
+    s = f32x16{};
+    const uint16_t* krow = ks + (32 * kb + col) * D;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const uint16_t* krow = ks + (32 * kb + col) * D;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * c + h) ^ k_sw));
-        s[kb] = mfma32(av, qa[c], s[kb]);
-      }
+    for (int c = 0; c < NC; ++c) {
+      const u32x4 av = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * c + h) ^ k_sw));
+      s = mfma32(av, qa[c], s);
     }
-    if (masked) {
-      // i - j = t - rc(r) with t per lane and tile, rc(r) = 8(r/4) + r%4 a compile-time row
-      // constant: each test compares a constant with one threshold.
-      const int t0 = qi - j0 - 4 * h;
+  };
+  auto mask = [&](f32x16& s, int j0, int kb, int lo_rel, bool local_pass) __attribute__((always_inline)) {
+    // i - j = t - rc(r) with t per lane and half tile, rc(r) = 8(r/4) + r%4 a compile-time row
+    // constant: each test compares a constant with one threshold.
+    const int t = qi - j0 - 32 * kb - 4 * h;
+    const int keep_le = t - lo_rel;  // i - j >= lo_rel  <=>  rc <= keep_le
+    const int drop_le = t - w0;      // i - j <  w0      <=>  rc >  drop_le
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int t = t0 - 32 * kb;
-        const int keep_le = t - lo_rel;  // i - j >= lo_rel  <=>  rc <= keep_le
-        const int drop_le = t - w0;      // i - j <  w0      <=>  rc >  drop_le
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rc = 8 * (r >> 2) + (r & 3);
-          const bool keep = (rc <= keep_le) && (!local_pass || rc > drop_le);
-          if (!keep) s[kb][r] = kNegBig;
-        }
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int rc = 8 * (r >> 2) + (r & 3);
+      const bool keep = (rc <= keep_le) && (!local_pass || rc > drop_le);
+      if (!keep) s[r] = kNegBig;
     }
-    float mx = kNegBig;
+  };
+  auto exps = [&](const f32x16& s, u32x4 (&pb)[2]) __attribute__((always_inline)) {
+    float ps = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[kb][r], s[kb][r + 1]);
-    mx = pair_max(mx);
-    const bool up = mx > m_run + kSlack;
-    if (wave_any(up)) {
-      const float m_new = up ? mx : m_run;
+      for (int w = 0; w < 4; ++w) {
+        const int r = 8 * ch + 2 * w;
+        const uint32_t pk = pack_bf16x2(fast_exp2(s[r] - m_run), fast_exp2(s[r + 1] - m_run));
+        pb[ch][w] = pk;
+        ps = sum_bf16x2(pk, ps);
+      }
+    return ps;
+  };
+  // Online softmax of one half tile: exponentials against the stored max; when some score
+  // exceeds it by more than kSlack (always on a row's first tile), raise the max to the column's,
+  // rescale O and the sums, and redo the exponentials. Adds the row sum to the pass's weight.
+  auto softmax = [&](const f32x16& s, u32x4 (&pb)[2], bool local_pass) __attribute__((always_inline)) {
+    float mxl = kNegBig;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mxl = max3f(mxl, s[r], s[r + 1]);
+    float ps = exps(s, pb);
+    if (wave_any(mxl > m_run + kSlack)) {
+      const float m_new = __builtin_fmaxf(m_run, pair_max(mxl));
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_pass[0] *= alpha;
       l_pass[1] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      ps = exps(s, pb);
     }
-    u32x4 pb[2][2];  // [kb][chunk] bf16 P^T operands
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int r = 8 * ch + 2 * w;
-          const uint32_t pk = pack_bf16x2(fast_exp2(s[kb][r] - m_run), fast_exp2(s[kb][r + 1] - m_run));
-          pb[kb][ch][w] = pk;
-          ps = sum_bf16x2(pk, ps);
-        }
     l_pass[local_pass ? 0 : 1] += ps;
+  };
+  auto pv = [&](const uint16_t* vs, int kb, const u32x4 (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int ch = 0; ch < 2; ++ch) {
+      const int key0 = 32 * kb + 16 * ch + tr_key, key1 = key0 + 8;
+      const uint16_t* r0 = vs + key0 * D;
+      const uint16_t* r1 = vs + key1 * D;
+      const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        const int key0 = 32 * kb + 16 * ch + tr_key, key1 = key0 + 8;
-        const uint16_t* r0 = vs + key0 * D;
-        const uint16_t* r1 = vs + key1 * D;
-        const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = 32 * db + tr_d;
-          const u32x2 v0 = read_tr(r0 + 8 * ((d >> 3) ^ sw0) + (d & 7));
-          const u32x2 v1 = read_tr(r1 + 8 * ((d >> 3) ^ sw1) + (d & 7));
-          o[db] = mfma32(u32x4{v0[0], v0[1], v1[0], v1[1]}, pb[kb][ch], o[db]);
-        }
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + tr_d;
+        const u32x2 v0 = read_tr(r0 + 8 * ((d >> 3) ^ sw0) + (d & 7));
+        const u32x2 v1 = read_tr(r1 + 8 * ((d >> 3) ^ sw1) + (d & 7));
+        o[db] = mfma32(u32x4{v0[0], v0[1], v1[0], v1[1]}, pb[ch], o[db]);
       }
+    }
   };
 
-  // One pass over n tiles kt = kt_first, kt_first-1, ..., with tile t+1 in flight while tile t
-  // is computed; the loop is unrolled by two so each step names its LDS buffers statically.
-  // `active`: this wave has pairs of the pass in the tile; `masked`: some pair of the tile
-  // needs the index mask.
+  // One half step in 16 slots of one MFMA each: slots 0-7 are the score MFMAs of the next half
+  // tile (K rows 32*kb_k.. of ks into s_out, when DO_QK), slots 8-15 the PV MFMAs of the
+  // previous half tile (P^T pb_prev, V rows 32*kb_v.. of vs, when DO_PV). Between them go the
+  // softmax VALU of the current half tile (s_cur -> pb_cur, the exponentials against the stored
+  // max; they need none of these MFMAs) and the LDS operand reads two slots ahead.
+  // sched_barrier keeps the slot order, so the matrix unit and the VALU work side by side.
+  // The rescale check closes the step.
+  auto half_step = [&](auto do_qk, auto do_pv, const uint16_t* ks, int kb_k, const u32x4 (&qa)[NC], f32x16& s_out,
+                       const uint16_t* vs, int kb_v, const u32x4 (&pb_prev)[2], const f32x16& s_cur,
+                       u32x4 (&pb_cur)[2], bool local_pass) __attribute__((always_inline)) {
+    constexpr bool DO_QK = decltype(do_qk)::value, DO_PV = decltype(do_pv)::value;
+    constexpr int NS = NC + 2 * NDB;  // slots: NC score MFMAs, then 2 * NDB PV MFMAs
+    const uint16_t* krow = ks + (32 * kb_k + col) * D;
+    auto read_k = [&](int c) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * c + h) ^ k_sw));
+    };
+    auto read_v = [&](int i) __attribute__((always_inline)) {
+      const int ch = i / NDB, db = i % NDB;
+      const int key0 = 32 * kb_v + 16 * ch + tr_key, key1 = key0 + 8;
+      const int d = 32 * db + tr_d;
+      const u32x2 v0 = read_tr(vs + key0 * D + 8 * ((d >> 3) ^ swz<D>(key0)) + (d & 7));
+      const u32x2 v1 = read_tr(vs + key1 * D + 8 * ((d >> 3) ^ swz<D>(key1)) + (d & 7));
+      return u32x4{v0[0], v0[1], v1[0], v1[1]};
+    };
+    // Operand of slot m (K chunk m for m < NC, V block m - NC after).
+    auto read_op = [&](int m) __attribute__((always_inline)) {
+      if (m < NC) return DO_QK ? read_k(m) : u32x4{0, 0, 0, 0};
+      return DO_PV ? read_v(m - NC) : u32x4{0, 0, 0, 0};
+    };
+    if (DO_QK) s_out = f32x16{};
+    constexpr int AHEAD = 3;  // operand reads run this many slots ahead of their MFMA
+    u32x4 op[NS];
+#pragma unroll
+    for (int m = 0; m < AHEAD; ++m) op[m] = read_op(m);
+    float mxl = kNegBig, ps = 0.f, e0 = 0.f, e1 = 0.f;
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (m < NC) {
+        if (DO_QK) s_out = mfma32(op[m], qa[m], s_out);
+      } else {
+        const int i = m - NC;
+        if (DO_PV) o[i % NDB] = mfma32(op[m], pb_prev[i / NDB], o[i % NDB]);
+      }
+      if (m + AHEAD < NS) op[m + AHEAD] = read_op(m + AHEAD);
+      // Softmax VALU chunks 16m/NS .. 16(m+1)/NS - 1: chunk 2p computes the exponentials of score
+      // pair p, chunk 2p+1 packs them, adds them to the row sum and folds them into the max.
+#pragma unroll
+      for (int k = (16 * m) / NS; k < (16 * (m + 1)) / NS; ++k) {
+        const int pr = k >> 1, r = 2 * pr;
+        if ((k & 1) == 0) {
+          e0 = fast_exp2(s_cur[r] - m_run);
+          e1 = fast_exp2(s_cur[r + 1] - m_run);
+        } else {
+          const uint32_t pk = pack_bf16x2(e0, e1);
+          // Pin the value to its slot: the compiler would otherwise sink the exponentials past
+          // the rescale check (whose slow path recomputes them) and out of the MFMA slots.
+          asm volatile("" ::"v"(pk));
+          pb_cur[pr >> 2][pr & 3] = pk;
+          ps = sum_bf16x2(pk, ps);
+          mxl = max3f(mxl, s_cur[r], s_cur[r + 1]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (wave_any(mxl > m_run + kSlack)) {
+      const float m_new = __builtin_fmaxf(m_run, pair_max(mxl));
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_pass[0] *= alpha;
+      l_pass[1] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      ps = exps(s_cur, pb_cur);
+    }
+    l_pass[local_pass ? 0 : 1] += ps;
+  };
+
+  // One pass over n tiles kt = kt_first, kt_first-1, ... (tile t has keys j0(t) .. +63),
+  // software-pipelined over 32-key halves inside each wave so the softmax VALU of one half runs
+  // while the matrix unit works on its neighbours:
+  //   half step (t,0): softmax(t,0) beside qk(t,1) [K_t] and pv(t-1,1) [V_{t-1}];
+  //   barrier t; loads of K_{t+2} and V_{t+1} into the buffers of K_t and V_{t-1};
+  //   half step (t,1): softmax(t,1) beside qk(t+1,0) [K_{t+1}] and pv(t,0) [V_t].
+  // Every buffer a load targets was last read before the barrier that precedes the load, and the
+  // loads are waited before the next barrier, a half step before the tile is read. Tiles where
+  // this wave has no pair of the pass, or that need the index mask, are masked (all pairs masked
+  // for the former). The first and last tiles are peeled (no pv before the first half, no qk
+  // after the last), and the loop is unrolled by two so each step names its LDS buffers
+  // statically.
   auto run_pass = [&](int kt_first, int n, const u32x4 (&qa)[NC], const uint16_t* ksrc, bool rotate_k,
                       bool local_pass, int lo_rel) __attribute__((always_inline)) {
     auto j0_of = [&](int t) { return (kt_first - t) * kBN; };
-    u32x4 flo, fhi;
-    if (rotate_k) {
-      fetch_k(j0_of(0), flo, fhi);
-      commit_k(j0_of(0), s_k0, flo, fhi);
-    } else {
-      stage_direct(ksrc, s_k0, j0_of(0));
-    }
-    stage_direct(vbase, s_v0, j0_of(0));
-    wait_loads();
-    __syncthreads();
-    auto step = [&](int t, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
-      const bool more = t + 1 < n;
-      if (more) {
-        if (rotate_k) fetch_k(j0_of(t + 1), flo, fhi);
-        else stage_direct(ksrc, kn, j0_of(t + 1));
-        stage_direct(vbase, vn, j0_of(t + 1));
-      }
+    // True when tile t needs the index mask for this wave (some pair masked, or none active).
+    auto needs_mask = [&](int t) __attribute__((always_inline)) {
       const int j0 = j0_of(t);
       const int w_max = iw_last - j0, w_min = iw - (j0 + kBN - 1);
+      const bool masked = local_pass ? !(w_min >= 0 && w_max < w0) : (w_min < w0);
       const bool active = wave_live && (local_pass ? (w_max >= 0 && w_min < w0) : (w_max >= w0));
-      if (active) {
-        const bool masked = local_pass ? !(w_min >= 0 && w_max < w0) : (w_min < w0);
-        if (masked) tile_step(kc, vc, qa, j0, true, lo_rel, local_pass);
-        else tile_step(kc, vc, qa, j0, false, lo_rel, local_pass);
-      }
-      if (more && rotate_k) commit_k(j0_of(t + 1), kn, flo, fhi);
+      return masked || !active;
+    };
+    u32x4 flo, fhi;
+    auto load_k = [&](int t, uint16_t* dst) __attribute__((always_inline)) {
+      if (rotate_k) fetch_k(j0_of(t), flo, fhi);
+      else stage_direct(ksrc, dst, j0_of(t));
+    };
+    auto finish_k = [&](int t, uint16_t* dst) __attribute__((always_inline)) {
+      if (rotate_k) commit_k(j0_of(t), dst, flo, fhi);
+    };
+    // Prologue: K_0, K_1 and V_0 staged (V_0 into both V buffers, so the first tile's PV of a
+    // "previous" half with P^T = 0 reads finite values and adds nothing); scores of half (0,0).
+    load_k(0, s_k0);
+    finish_k(0, s_k0);
+    if (n > 1) {
+      load_k(1, s_k1);
+      finish_k(1, s_k1);
+    }
+    stage_direct(vbase, s_v0, j0_of(0));
+    stage_direct(vbase, s_v1, j0_of(0));
+    wait_loads();
+    __syncthreads();
+    f32x16 s0, s1;          // scores of the current tile's halves
+    u32x4 p0[2], p1[2];     // P^T of half 0 (this tile) and half 1 (previous tile, then this)
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) p1[ch] = u32x4{0, 0, 0, 0};
+    qk(s_k0, 0, qa, s0);
+    const std::true_type yes{};
+    // Every half step runs all three parts: the first tile's pv(-1, 1) adds P^T = 0, and the last
+    // tile's qk(n, 0) reads a stale buffer into scores nobody uses.
+    auto tile = [&](int t, const uint16_t* k_cur, uint16_t* k_other, const uint16_t* v_prev, uint16_t* v_cur)
+                    __attribute__((always_inline)) {
+      // k_cur = K_t; k_other = K_{t+1} now, refilled with K_{t+2}; v_prev = V_{t-1}, refilled with
+      // V_{t+1}; v_cur = V_t.
+      const bool msk = needs_mask(t);
+      // half step (t, 0)
+      if (msk) mask(s0, j0_of(t), 0, lo_rel, local_pass);
+      half_step(yes, yes, k_cur, 1, qa, s1, v_prev, 1, p1, s0, p0, local_pass);
+      if (t + 1 < n && rotate_k) finish_k(t + 1, k_other);  // fused mode: K_{t+1} rotated into LDS
       wait_loads();
       __syncthreads();
+      if (t + 2 < n) load_k(t + 2, const_cast<uint16_t*>(k_cur));
+      if (t + 1 < n) stage_direct(vbase, const_cast<uint16_t*>(v_prev), j0_of(t + 1));
+      // half step (t, 1)
+      if (msk) mask(s1, j0_of(t), 1, lo_rel, local_pass);
+      half_step(yes, yes, k_other, 0, qa, s0, v_cur, 0, p0, s1, p1, local_pass);
     };
     int t = 0;
     for (; t + 1 < n; t += 2) {
-      step(t, s_k0, s_v0, s_k1, s_v1);
-      step(t + 1, s_k1, s_v1, s_k0, s_v0);
+      tile(t, s_k0, s_k1, s_v1, s_v0);
+      tile(t + 1, s_k1, s_k0, s_v0, s_v1);
     }
-    if (t < n) step(t, s_k0, s_v0, s_k1, s_v1);
+    if (t < n) tile(t, s_k0, s_k1, s_v1, s_v0);
+    // Drain: PV of the last half; V_{n-1} sits in buffer (n-1) % 2.
+    if ((n - 1) & 1) pv(s_v1, 1, p1);
+    else pv(s_v0, 1, p1);
+    __syncthreads();  // the next pass's prologue refills the buffers
   };
 
   // ---------------- pass A: local pairs, tiles n_kt-1 down to kt_lo ----------------
