@@ -99,22 +99,15 @@ void decode_split_kernel(const DecodeArgs<D> a) {
     for (int c = 0; c < NQC; ++c)
       if (!q_live) raw[c] = u32x4{0, 0, 0, 0};
   };
-  u32x4 qr[NQC], qs[NQC];
-  {
-    u32x4 raw[NQC];
-    load_q(raw);
-    mask_q(raw);
+  // The q loads are issued first; they are finished (scaled, rotated) after the first block's K
+  // and V loads are in flight, so the first cache block does not wait for them.
+  u32x4 qr[NQC], qs[NQC], qraw[NQC];
+  load_q(qraw);
+  uint32_t wq[NQC / 2][8];  // phase increments of this lane's query pairs
 #pragma unroll
-    for (int c = 0; c < NQC; ++c) qs[c] = scale8(raw[c], a.scale_log2);
-    const int dq = correction_offset(p, G);
+  for (int c = 0; c < NQC / 2; ++c)
 #pragma unroll
-    for (int c = 0; c < NQC / 2; ++c) {
-      u32x4 lo = raw[c], hi = raw[c + NQC / 2];
-      rotate8_scaled(lo, hi, dq, &a.W[32 * c + 8 * lg], a.scale_log2);
-      qr[c] = lo;
-      qr[c + NQC / 2] = hi;
-    }
-  }
+    for (int e = 0; e < 8; ++e) wq[c][e] = a.W[32 * c + 8 * lg + e];
 
   const size_t row_stride = (size_t)a.Hkv * D;
   const uint16_t* kbase = a.kc + (size_t)b * a.cap * row_stride + (size_t)gl * D;
@@ -291,6 +284,20 @@ void decode_split_kernel(const DecodeArgs<D> a) {
   u32x4 ka[NKR], kb[NKR];
   load_v(k_begin, B0);
   load_k(k_begin, ka);
+  wait_vmcnt<NKR + NLD>();  // q and its phase increments are in; block 0 stays in flight
+  mask_q(qraw);
+#pragma unroll
+  for (int c = 0; c < NQC; ++c) qs[c] = scale8(qraw[c], a.scale_log2);
+  {
+    const int dq = correction_offset(p, G);
+#pragma unroll
+    for (int c = 0; c < NQC / 2; ++c) {
+      u32x4 lo = qraw[c], hi = qraw[c + NQC / 2];
+      rotate8_scaled(lo, hi, dq, wq[c], a.scale_log2);
+      qr[c] = lo;
+      qr[c + NQC / 2] = hi;
+    }
+  }
   if (need_table) fill_table(k_begin, B0);
   lds_barrier();
   // MORE: a block i+1 exists (always true except for the chunk's last block).
@@ -340,45 +347,52 @@ void decode_split_kernel(const DecodeArgs<D> a) {
 }
 
 // Reduce: one workgroup of 256 threads per (query head, 32-wide slice of d, batch). Thread t
-// owns splits t, t+256, ...; all of its partial loads are issued up front, then the block max of
-// the split maxima, the weights exp2(m_s - M), and the weighted sums of 32 outputs are reduced
-// across the 4 waves through LDS.
+// merges splits t, t+256, ... by an online log-sum-exp (one load round trip when there are at
+// most 256 splits); the workgroup then takes the block max of the thread maxima, rescales each
+// thread's (sum, 32 outputs) to it and adds them up across the 4 waves through LDS.
 constexpr int kRedThreads = 256;
 
 template <int D>
 __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
                                                                     float* __restrict__ lse, int Hq, int n_splits) {
-  __shared__ float s_red[kRedThreads / 64];
+  __shared__ float s_m[kRedThreads / 64];
   __shared__ float s_acc[kRedThreads / 64][33];
   const int head = blockIdx.x, slice = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const float* src = ws + ((size_t)b * Hq + head) * n_splits * (D + 2);
-  // Pass 1: maxima of this thread's splits.
-  float m = kNegBig;
-  for (int s = t; s < n_splits; s += kRedThreads) m = fmaxf(m, src[(size_t)s * (D + 2)]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) s_red[wave] = m;
-  __syncthreads();
-  float M = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kRedThreads / 64; ++w) M = fmaxf(M, s_red[w]);
-  // Pass 2: weighted sums of the denominators and of this slice's 32 outputs.
-  float den = 0.f, acc[32];
+  float m = kNegBig, den = 0.f, acc[32];
 #pragma unroll
   for (int d = 0; d < 32; ++d) acc[d] = 0.f;
-  for (int s = t; s < n_splits; s += kRedThreads) {
-    const float* ps = src + (size_t)s * (D + 2);
-    const float w = fast_exp2(ps[0] - M);
-    den += w * ps[1];
+  for (int sp = t; sp < n_splits; sp += kRedThreads) {
+    const float* ps = src + (size_t)sp * (D + 2);
+    const float ms = ps[0], ls = ps[1];
+    f32x4 v[8];
     const f32x4* pv = reinterpret_cast<const f32x4*>(ps + 2 + 32 * slice);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const f32x4 v = pv[q];
+    for (int q = 0; q < 8; ++q) v[q] = pv[q];
+    const float mn = fmaxf(m, ms);
+    const float a = fast_exp2(m - mn), w = fast_exp2(ms - mn);
+    m = mn;
+    den = den * a + w * ls;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * q + e] += w * v[e];
-    }
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * q + e] = acc[4 * q + e] * a + w * v[q][e];
   }
+  // Block max of the thread maxima.
+  float M = m;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) s_m[wave] = M;
+  __syncthreads();
+  M = s_m[0];
+#pragma unroll
+  for (int w = 1; w < kRedThreads / 64; ++w) M = fmaxf(M, s_m[w]);
+  // Rescale to the block max and sum.
+  const float f = fast_exp2(m - M);
+  den *= f;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) acc[d] *= f;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     den += __shfl_xor(den, off);
