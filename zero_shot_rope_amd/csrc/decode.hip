@@ -347,20 +347,23 @@ void decode_split_kernel(const DecodeArgs<D> a) {
 }
 
 // Reduce: one workgroup of 256 threads per (query head, 32-wide slice of d, batch). Thread t
-// merges splits t, t+256, ... by an online log-sum-exp (one load round trip when there are at
-// most 256 splits); the workgroup then takes the block max of the thread maxima, rescales each
-// thread's (sum, 32 outputs) to it and adds them up across the 4 waves through LDS.
+// takes splits t, t+256, ... : it loads each one's (max, sum, 32 outputs) at once (a single load
+// round trip for up to 256 splits) and merges them by an online log-sum-exp. One shuffle tree
+// and LDS give the block max M; each thread writes its sum and outputs rescaled to M into LDS,
+// and two LDS stages (8 groups of 32 rows, then the 8 group sums) add them up.
 constexpr int kRedThreads = 256;
+constexpr int kRedGroups = kRedThreads / 32;
 
 template <int D>
 __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
                                                                     float* __restrict__ lse, int Hq, int n_splits) {
   __shared__ float s_m[kRedThreads / 64];
-  __shared__ float s_acc[kRedThreads / 64][33];
+  __shared__ float s_row[kRedThreads][33];  // per thread: 32 rescaled outputs, then the rescaled sum
+  __shared__ float s_grp[kRedGroups][33];
   const int head = blockIdx.x, slice = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const float* src = ws + ((size_t)b * Hq + head) * n_splits * (D + 2);
-  float m = kNegBig, den = 0.f, acc[32];
+  float m = kNegBig, l = 0.f, acc[32];
 #pragma unroll
   for (int d = 0; d < 32; ++d) acc[d] = 0.f;
   for (int sp = t; sp < n_splits; sp += kRedThreads) {
@@ -373,13 +376,12 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
     const float mn = fmaxf(m, ms);
     const float a = fast_exp2(m - mn), w = fast_exp2(ms - mn);
     m = mn;
-    den = den * a + w * ls;
+    l = l * a + w * ls;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[4 * q + e] = acc[4 * q + e] * a + w * v[q][e];
   }
-  // Block max of the thread maxima.
   float M = m;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -388,32 +390,34 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
   M = s_m[0];
 #pragma unroll
   for (int w = 1; w < kRedThreads / 64; ++w) M = fmaxf(M, s_m[w]);
-  // Rescale to the block max and sum.
   const float f = fast_exp2(m - M);
-  den *= f;
 #pragma unroll
-  for (int d = 0; d < 32; ++d) acc[d] *= f;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    den += __shfl_xor(den, off);
-#pragma unroll
-    for (int d = 0; d < 32; ++d) acc[d] += __shfl_xor(acc[d], off);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int d = 0; d < 32; ++d) s_acc[wave][d] = acc[d];
-    s_acc[wave][32] = den;
+  for (int d = 0; d < 32; ++d) s_row[t][d] = acc[d] * f;
+  s_row[t][32] = l * f;
+  __syncthreads();
+  {
+    // Thread (g, c): column c (32 = the sum) of rows 32g .. 32g+31.
+    const int g = t >> 5, c = t & 31;
+    float x = 0.f, y = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < 32; ++r) x += s_row[32 * g + r][c];
+    s_grp[g][c] = x;
+    if (c == 0) {
+#pragma unroll 8
+      for (int r = 0; r < 32; ++r) y += s_row[32 * g + r][32];
+      s_grp[g][32] = y;
+    }
   }
   __syncthreads();
   if (t < 32) {
-    float tot = 0.f, dtot = 0.f;
+    float tot = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kRedThreads / 64; ++w) {
-      tot += s_acc[w][t];
-      dtot += s_acc[w][32];
+    for (int g = 0; g < kRedGroups; ++g) {
+      tot += s_grp[g][t];
+      den += s_grp[g][32];
     }
-    o[((size_t)b * Hq + head) * D + 32 * slice + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(tot / dtot));
-    if (lse != nullptr && slice == 0 && t == 0) lse[(size_t)b * Hq + head] = (M + __log2f(dtot)) * 0.69314718055994531f;
+    o[((size_t)b * Hq + head) * D + 32 * slice + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(tot / den));
+    if (lse != nullptr && slice == 0 && t == 0) lse[(size_t)b * Hq + head] = (M + __log2f(den)) * 0.69314718055994531f;
   }
 }
 
