@@ -82,6 +82,30 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
                     int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunked prefill (prefill against a cache prefix): q_len query rows at absolute positions
+ * q_offset .. L - 1 attend keys 0 .. L - 1 of a base-position cache, L = q_offset + q_len, with
+ * G = max(1, ceil(L / w_pretrained)) from this L (review page, Method: G follows the current
+ * length, so a stream of chunks crosses length boundaries with no cache rewrite; gist.science
+ * summary, Methodologie section 2: the cache keeps base positions and the correction is applied
+ * in registers). Row r equals row q_offset + r of bifocal_prefill over the first L positions.
+ *   q        [batch, q_len, n_q_heads, head_dim] bf16, post-base-RoPE at positions q_offset + r
+ *   k_cache  [batch, cache_capacity, n_kv_heads, head_dim] bf16, positions 0 .. L-1 valid (the
+ *            chunk's own keys already written at q_offset .. L-1); read only
+ *   v_cache  same layout as k_cache
+ *   o        [batch, q_len, n_q_heads, head_dim] bf16, written
+ *   lse      [batch, n_q_heads, q_len] float32, written when not NULL
+ *   workspace / workspace_bytes: as for bifocal_prefill, sized for L:
+ *            >= bifocal_prefill_workspace_bytes(batch, n_kv_heads, head_dim, q_offset + q_len)
+ *            (the corrected keys of positions 0 .. L-1, compact [batch, L, n_kv_heads, head_dim]).
+ * q_offset = 0 with q_len = cache_capacity is bifocal_prefill. Requires q_len >= 1,
+ * q_offset >= 0, q_offset + q_len <= cache_capacity <= 2^30; other limits as bifocal_prefill.
+ * Returns BIFOCAL_OK or a negative bifocal_status. */
+int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                          int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                          int64_t q_len, int64_t q_offset, int64_t cache_capacity,
+                          int64_t w0, int64_t w_pretrained, double rope_theta,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace bifocal_decode needs for any L <= max_L with these shapes.
  * Returns 0 for invalid arguments (which bifocal_decode would reject anyway). */
 size_t bifocal_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,

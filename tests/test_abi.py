@@ -88,6 +88,27 @@ def test_prefill_rejects_before_any_hip_call(lib, kw, expect):
     assert prefill_call(lib, **kw) == expect
 
 
+def chunk_call(lib, **kw):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, batch=1, hq=4, hkv=2, d=128, q_len=100, q_off=50, cap=200,
+                w0=32, wp=64, theta=1e4, ws=None, wsb=0)
+    args.update(kw)
+    return lib.bifocal_prefill_chunk(args["q"], args["kc"], args["vc"], args["o"], args["lse"], args["batch"], args["hq"],
+                                     args["hkv"], args["d"], args["q_len"], args["q_off"], args["cap"], args["w0"],
+                                     args["wp"], args["theta"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), EINVAL), (dict(kc=None), EINVAL), (dict(vc=None), EINVAL), (dict(o=None), EINVAL),
+    (dict(q_len=0), EINVAL), (dict(q_off=-1), EINVAL), (dict(q_off=101), EINVAL), (dict(q_len=201, q_off=0), EINVAL),
+    (dict(cap=0), EINVAL), (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL), (dict(theta=0.0), EINVAL),
+    (dict(hq=6, hkv=4), EINVAL), (dict(batch=0), EINVAL), (dict(d=96), EUNSUP),
+    (dict(cap=(1 << 30) + 1, q_off=0), EUNSUP),
+    (dict(ws=FAKE, wsb=150 * 2 * 128 * 2 - 1), EWS),   # sized for L = q_off + q_len = 150
+])
+def test_prefill_chunk_rejects_before_any_hip_call(lib, kw, expect):
+    assert chunk_call(lib, **kw) == expect
+
+
 def decode_call(lib, **kw):
     args = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, batch=1, hq=8, hkv=2, d=128, L=100, cap=128,
                 w0=16, wp=32, theta=1e4, ws=FAKE, wsb=1 << 40)

@@ -199,6 +199,81 @@ def test_prefill_qwen3_8b_128k(mode):
 
 
 # ---------------------------------------------------------------------------------------
+# Chunked prefill: query rows at an offset against a cache prefix
+# ---------------------------------------------------------------------------------------
+def run_chunk(q_bits, k_bits, v_bits, q_offset, w0, wp, theta, mode="prerotated"):
+    q, kc, vc = dev(q_bits), dev(k_bits), dev(v_bits)
+    B, Lq, Hq, D = q.shape
+    L = q_offset + Lq
+    obuf, o = guarded((B, Lq, Hq, D), torch.bfloat16)
+    lbuf, lse = guarded((B, Hq, Lq), torch.float32)
+    ws = None
+    if mode == "prerotated":
+        nws = Z.bifocal_prefill_workspace_bytes(B, kc.shape[2], D, L)
+        wbuf = torch.full((nws + GUARD,), 0x5A, dtype=torch.uint8, device="cuda")
+        ws = wbuf[:nws]
+    Z.prefill_chunk(q, kc, vc, q_offset=q_offset, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse,
+                    workspace=ws)
+    torch.cuda.synchronize()
+    assert_guard(obuf, o.numel())
+    assert_guard(lbuf, lse.numel())
+    if ws is not None:
+        assert torch.all(wbuf[nws:] == 0x5A), "write outside the workspace"
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+SMALL_CHUNK = [
+    # (batch, cap, Hq, Hkv, D, w_pretrained, w0, theta, [(q_offset, q_len), ...])
+    (1, 1000, 4, 2, 128, 128, 64, 1e6, [(0, 300), (300, 200), (500, 1), (444, 556)]),  # G 3, 4, 4, 8
+    (2, 700, 8, 2, 64, 100, 33, 1e4, [(0, 700), (64, 64), (129, 300), (650, 50)]),
+    (1, 900, 32, 8, 128, 200, 100, 1e6, [(700, 200), (0, 1)]),                        # Qwen3-8B heads
+    (1, 500, 4, 1, 128, 1000, 50, 1e6, [(100, 400)]),                                # G = 1
+    (1, 600, 4, 4, 64, 64, 0, 1e4, [(200, 300)]),                                    # w0 = 0
+    (1, 800, 8, 1, 128, 64, 700, 1e4, [(600, 200)]),                                 # 8:1 GQA, wide band
+]
+
+
+@pytest.mark.parametrize("mode", ["prerotated", "fused"])
+@pytest.mark.parametrize("case", SMALL_CHUNK, ids=[f"B{c[0]}cap{c[1]}H{c[2]}-{c[3]}D{c[4]}w{c[6]}" for c in SMALL_CHUNK])
+def test_prefill_chunk_small(case, mode):
+    B, cap, Hq, Hkv, D, wp, w0, theta, chunks = case
+    rng = np.random.default_rng(cap + Hq + D)
+    kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    qall = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hq, D), dtype=np.float32))  # query of every position
+    for q_offset, q_len in chunks:
+        L = q_offset + q_len
+        say(f"prefill chunk {case[:8]} offset={q_offset} len={q_len} G={group_size(L, wp)} {mode}")
+        o, lse = run_chunk(qall[:, q_offset:L], kb, vb, q_offset, w0, wp, theta, mode)
+        ref_o, ref_lse = bifocal_attention(f64(qall[:, :L]), f64(kb[:, :L]), f64(vb[:, :L]), w0=w0, w_pretrained=wp,
+                                           theta=theta, rows=np.arange(q_offset, L))
+        compare(o, ref_o, f"o offset={q_offset}")
+        assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
+
+
+def test_prefill_chunk_of_whole_sequence_is_prefill():
+    B, L, Hq, Hkv, D, wp, w0, theta = 1, 650, 8, 2, 128, 200, 60, 1e6
+    bits = W.random_case(91, B, L, Hq, Hkv, D)
+    o_pre, lse_pre = run_prefill(bits, w0, wp, theta)
+    o_chk, lse_chk = run_chunk(bits["q"], bits["k"], bits["v"], 0, w0, wp, theta)
+    assert np.array_equal(o_pre, o_chk) and np.array_equal(lse_pre, lse_chk)
+
+
+def test_prefill_chunk_qwen3_8b_last_4k():
+    cfg = W.QWEN3_8B_128K
+    q_offset, q_len = cfg.L - 4096, 4096
+    say(f"prefill chunk {cfg.name}: rows {q_offset}..{cfg.L - 1} against the 128K cache (sampled rows)")
+    bits = W.prefill_inputs(cfg)
+    o, lse = run_chunk(bits["q"][:, q_offset:], bits["k"], bits["v"], q_offset, cfg.w0, cfg.w_pretrained,
+                       cfg.rope_theta)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = sample_rows(q_len, 64, 4, seed=43, n_random=12) + q_offset
+    ref_o, ref_lse = _oracle_rows(bits, cfg, rows)
+    compare(o[:, rows - q_offset], ref_o, "o(sampled rows)")
+    assert np.max(np.abs(lse[:, :, rows - q_offset] - ref_lse)) <= LSE_ABS
+
+
+# ---------------------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------------------
 def run_decode(q_bits, k_bits, v_bits, L, w0, wp, theta, workspace=None):

@@ -21,6 +21,7 @@ EXPORTED_SYMBOLS = (
     "bifocal_group_size",
     "bifocal_prefill_workspace_bytes",
     "bifocal_prefill",
+    "bifocal_prefill_chunk",
     "bifocal_decode_workspace_bytes",
     "bifocal_decode",
     "bifocal_positions",
@@ -58,6 +59,9 @@ def load_library():
         lib.bifocal_prefill.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
                                         c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
         lib.bifocal_prefill.restype = c_int
+        lib.bifocal_prefill_chunk.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
+                                              c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
+        lib.bifocal_prefill_chunk.restype = c_int
         lib.bifocal_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_i64]
         lib.bifocal_decode_workspace_bytes.restype = c_sz
         lib.bifocal_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
@@ -124,6 +128,18 @@ def bifocal_prefill(q, k, v, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, 
         raise BifocalError(st, "bifocal_prefill")
 
 
+def bifocal_prefill_chunk(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, q_len, q_offset,
+                          cache_capacity, w0, w_pretrained, rope_theta, workspace=None, workspace_bytes=0,
+                          stream=None) -> None:
+    lib = load_library()
+    st = lib.bifocal_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _fptr(lse), batch, n_q_heads,
+                                   n_kv_heads, head_dim, int(q_len), int(q_offset), int(cache_capacity), int(w0),
+                                   int(w_pretrained), float(rope_theta), _ptr(workspace), int(workspace_bytes),
+                                   _stream(stream))
+    if st != 0:
+        raise BifocalError(st, "bifocal_prefill_chunk")
+
+
 def bifocal_decode(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, cache_capacity,
                    w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream=None) -> None:
     lib = load_library()
@@ -180,6 +196,36 @@ def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_theta: float, out=None,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     bifocal_prefill(q, k, v, out, lse, B, Hq, k.shape[2], D, L, w0, w_pretrained, rope_theta, workspace, ws_bytes,
                     _stream(stream, q.device))
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def prefill_chunk(q, k_cache, v_cache, *, q_offset: int, w0: int, w_pretrained: int, rope_theta: float, out=None,
+                  lse=None, want_lse: bool = False, workspace=None, stream=None):
+    """q [B, Lq, Hq, D] at positions q_offset .. q_offset + Lq - 1 against caches [B, cap, Hkv, D]
+    holding positions 0 .. q_offset + Lq - 1 -> o [B, Lq, Hq, D] (and lse [B, Hq, Lq]).
+
+    `workspace`: None (single launch), a tensor (>= the workspace query for L = q_offset + Lq)
+    or "auto", as for prefill.
+    """
+    import torch
+
+    _check(q, "q", 4)
+    _check(k_cache, "k_cache", 4)
+    _check(v_cache, "v_cache", 4)
+    B, Lq, Hq, D = q.shape
+    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shapes do not match q")
+    L = int(q_offset) + Lq
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if isinstance(workspace, str) and workspace == "auto":
+        workspace = torch.empty(bifocal_prefill_workspace_bytes(B, Hkv, D, L), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    bifocal_prefill_chunk(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, Lq, q_offset, cap, w0, w_pretrained,
+                          rope_theta, workspace, ws_bytes, _stream(stream, q.device))
     return (out, lse) if (want_lse or lse is not None) else out
 
 

@@ -67,22 +67,14 @@ size_t bifocal_prefill_workspace_bytes(int batch, int n_kv_heads, int head_dim, 
   return bifocal::prefill_workspace_bytes(batch, L, n_kv_heads, head_dim);
 }
 
-int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
-                    int batch, int n_q_heads, int n_kv_heads, int head_dim,
-                    int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o) return BIFOCAL_EINVAL;
-  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
-  if (L < 1 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
-  if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
-  if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
-  if (L > kMaxL) return BIFOCAL_EUNSUPPORTED;
-  const long double elems = (long double)batch * (long double)L * n_q_heads * head_dim;
-  if (elems >= 4.0e18L) return BIFOCAL_EUNSUPPORTED;
-
+// Shared by the plain and the chunked prefill: query rows are positions L - Lq .. L - 1, keys
+// 0 .. L - 1 are read from k/v with kv_cap rows per batch. Arguments already validated.
+static int prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int n_q_heads,
+                        int n_kv_heads, int head_dim, int64_t L, int64_t Lq, int64_t kv_cap, int64_t w0,
+                        int64_t w_pretrained, double rope_theta, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (workspace != nullptr && workspace_bytes < bifocal_prefill_workspace_bytes(batch, n_kv_heads, head_dim, L))
     return BIFOCAL_EWORKSPACE;
-
   const int64_t G = bifocal_group_size(L, w_pretrained);
   uint32_t W[64];
   phase_increments(head_dim, rope_theta, W);
@@ -98,6 +90,8 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
   p.n_kv_heads = n_kv_heads;
   p.head_dim = head_dim;
   p.L = static_cast<int>(L);
+  p.Lq = static_cast<int>(Lq);
+  p.kv_cap = static_cast<int>(kv_cap);
   // G == 1 makes the correction rotation the identity, so every pair scores as a local one:
   // run the all-local path (the base model exactly, with no rotation work).
   p.w0 = (G == 1 || w0 >= L) ? static_cast<int>(L) : static_cast<int>(w0);
@@ -105,6 +99,41 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
   p.scale_log2 = scale_log2_for(head_dim);
   p.W = W;
   return map_hip(bifocal::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
+int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                    int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o) return BIFOCAL_EINVAL;
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
+  if (L < 1 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
+  if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
+  if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
+  if (L > kMaxL) return BIFOCAL_EUNSUPPORTED;
+  const long double elems = (long double)batch * (long double)L * n_q_heads * head_dim;
+  if (elems >= 4.0e18L) return BIFOCAL_EUNSUPPORTED;
+  return prefill_impl(q, k, v, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, L, L, w0, w_pretrained,
+                      rope_theta, workspace, workspace_bytes, stream);
+}
+
+int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                          int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                          int64_t q_len, int64_t q_offset, int64_t cache_capacity,
+                          int64_t w0, int64_t w_pretrained, double rope_theta,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !o) return BIFOCAL_EINVAL;
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
+  if (q_len < 1 || q_offset < 0 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
+  if (cache_capacity < 1 || q_offset > cache_capacity - q_len) return BIFOCAL_EINVAL;  // L <= capacity
+  if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
+  if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
+  if (cache_capacity > kMaxL) return BIFOCAL_EUNSUPPORTED;
+  const long double elems = (long double)batch * (long double)cache_capacity * n_q_heads * head_dim;
+  if (elems >= 4.0e18L) return BIFOCAL_EUNSUPPORTED;
+  const int64_t L = q_offset + q_len;
+  return prefill_impl(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, q_len,
+                      cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream);
 }
 
 size_t bifocal_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,

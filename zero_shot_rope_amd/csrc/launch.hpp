@@ -15,7 +15,9 @@ struct PrefillLaunch {
   void* o;
   float* lse;
   int batch, n_q_heads, n_kv_heads, head_dim;
-  int L;
+  int L;       // keys 0..L-1; the query rows are positions L - Lq .. L - 1
+  int Lq;      // query rows (L for a plain prefill)
+  int kv_cap;  // rows per batch in k and v (L for a plain prefill, the capacity for a cache)
   int w0;  // clamped to [0, L]
   int G;
   float scale_log2;      // log2(e) / sqrt(head_dim)

@@ -54,7 +54,10 @@ struct PrefillArgs {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  int B, Hq, Hkv, L;
+  int B, Hq, Hkv;
+  int L;       // keys 0..L-1 (the total length); query rows are the last Lq positions
+  int q0, Lq;  // absolute position of query row 0 (L - Lq) and the number of query rows
+  int kv_cap;  // rows per batch in k and v (the cache capacity; L for a plain prefill)
   int w0;  // clamped to [0, L]; w0 == L means every pair is local
   int G;
   int hpw;      // query heads per workgroup (1, 2 or 4)
@@ -119,7 +122,7 @@ void prefill_kernel(const PrefillArgs<D> a) {
   const int kvh = unit / upk;
   const int head = kvh * Hg + (unit % upk) * a.hpw + (wave % a.hpw);
   const int BM = 32 * (kWaves / a.hpw);
-  const int i0 = tile * BM;
+  const int i0 = a.q0 + tile * BM;  // absolute position of the tile's first query row
   const int iw = i0 + 32 * (wave / a.hpw);  // this wave's 32 query rows
   const int L = a.L, w0 = a.w0, G = a.G;
   const float qscale = a.scale_log2;
@@ -132,7 +135,7 @@ void prefill_kernel(const PrefillArgs<D> a) {
   // Query operand (B of S^T = K Q^T): lane (col, h) holds q[qi][16c + 8h .. +8], scaled into
   // log2 units; with `rotate` the correction rotation R(Delta_qi) is applied first.
   auto load_q = [&](bool rotate, u32x4 (&dst)[NC]) __attribute__((always_inline)) {
-    const uint16_t* src = a.q + ((size_t)b * L + qi) * q_row_stride + (size_t)head * D + 8 * h;
+    const uint16_t* src = a.q + ((size_t)b * a.Lq + (qi - a.q0)) * q_row_stride + (size_t)head * D + 8 * h;
     u32x4 raw[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -158,7 +161,8 @@ void prefill_kernel(const PrefillArgs<D> a) {
   const int iw_last = min(iw + 31, L - 1);
   const bool wave_live = iw <= L - 1;
   const size_t kv_row_stride = (size_t)a.Hkv * D;
-  const size_t kv_off = (size_t)b * L * kv_row_stride + (size_t)kvh * D;
+  const size_t kv_off = (size_t)b * a.kv_cap * kv_row_stride + (size_t)kvh * D;
+  const size_t krot_off = (size_t)b * L * kv_row_stride + (size_t)kvh * D;  // workspace K' is [B, L, Hkv, D]
   const uint16_t* kbase = a.k + kv_off;
   const uint16_t* vbase = a.v + kv_off;
 
@@ -463,7 +467,7 @@ void prefill_kernel(const PrefillArgs<D> a) {
     if (kt_hi > 0) {
       u32x4 qr[NC];
       load_q(true, qr);
-      if constexpr (MODE == kPrerotated) run_pass(kt_hi - 1, kt_hi, qr, a.krot + kv_off, false, false, w0);
+      if constexpr (MODE == kPrerotated) run_pass(kt_hi - 1, kt_hi, qr, a.krot + krot_off, false, false, w0);
       else run_pass(kt_hi - 1, kt_hi, qr, kbase, true, false, w0);
     }
   }
@@ -474,7 +478,7 @@ void prefill_kernel(const PrefillArgs<D> a) {
   const float den = w_a + w_r;
   const float inv = 1.0f / den;
   if (qi < L) {
-    uint16_t* dst = a.o + ((size_t)b * L + qi) * q_row_stride + (size_t)head * D;
+    uint16_t* dst = a.o + ((size_t)b * a.Lq + (qi - a.q0)) * q_row_stride + (size_t)head * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -485,30 +489,35 @@ void prefill_kernel(const PrefillArgs<D> a) {
         *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * g + 4 * h) = out;
       }
     if (a.lse != nullptr && h == 0)
-      a.lse[((size_t)b * a.Hq + head) * L + qi] = (m_run + __log2f(den)) * 0.69314718055994531f;
+      a.lse[((size_t)b * a.Hq + head) * a.Lq + (qi - a.q0)] = (m_run + __log2f(den)) * 0.69314718055994531f;
   }
 }
 
-// K' = R(Delta_j) K~ for every key row (prerotated mode): one thread per 8 rotation pairs.
+// K' = R(Delta_j) K~ for every key row j < L (prerotated mode): one thread per 8 rotation pairs.
+// Reads k with kv_cap rows per batch, writes the compact [B, L, Hkv, D] workspace.
 template <int D>
 __global__ __launch_bounds__(256) void rotate_keys_kernel(const uint16_t* __restrict__ k, uint16_t* __restrict__ kr,
-                                                          long long n_rows, int Hkv, int L, int G,
+                                                          long long n_rows, int Hkv, int L, int kv_cap, int G,
                                                           const PrefillArgs<D> a) {
   constexpr int HALF = D / 2, MCH = HALF / 8;
   const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
   if (u >= n_rows * MCH) return;
   const long long row = u / MCH;  // row = (b * L + j) * Hkv + g
   const int m = (int)(u % MCH);
-  const int j = (int)((row / Hkv) % L);
-  const size_t off = (size_t)row * D + 8 * m;
-  u32x4 lo = *reinterpret_cast<const u32x4*>(k + off);
-  u32x4 hi = *reinterpret_cast<const u32x4*>(k + off + HALF);
+  const long long bj = row / Hkv;
+  const int g = (int)(row % Hkv);
+  const int j = (int)(bj % L);
+  const long long bb = bj / L;
+  const size_t src = ((size_t)(bb * kv_cap + j) * Hkv + g) * D + 8 * m;
+  const size_t dst = (size_t)row * D + 8 * m;
+  u32x4 lo = *reinterpret_cast<const u32x4*>(k + src);
+  u32x4 hi = *reinterpret_cast<const u32x4*>(k + src + HALF);
   uint32_t w[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) w[e] = a.W[8 * m + e];
   rotate8(lo, hi, correction_offset(j, G), w);
-  *reinterpret_cast<u32x4*>(kr + off) = lo;
-  *reinterpret_cast<u32x4*>(kr + off + HALF) = hi;
+  *reinterpret_cast<u32x4*>(kr + dst) = lo;
+  *reinterpret_cast<u32x4*>(kr + dst + HALF) = hi;
 }
 
 template <int D>
@@ -524,12 +533,15 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
   a.Hq = p.n_q_heads;
   a.Hkv = p.n_kv_heads;
   a.L = p.L;
+  a.q0 = p.L - p.Lq;
+  a.Lq = p.Lq;
+  a.kv_cap = p.kv_cap;
   a.w0 = p.w0;
   a.G = p.G;
   const int Hg = p.n_q_heads / p.n_kv_heads;
   a.hpw = (Hg % 4 == 0) ? 4 : (Hg % 2 == 0) ? 2 : 1;
   const int BM = 32 * (kWaves / a.hpw);
-  a.n_tiles = (p.L + BM - 1) / BM;
+  a.n_tiles = (p.Lq + BM - 1) / BM;
   a.n_units = p.n_q_heads / a.hpw;
   a.scale_log2 = p.scale_log2;
   for (int i = 0; i < D / 2; ++i) a.W[i] = p.W[i];
@@ -543,7 +555,7 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
     const long long rows = (long long)p.batch * p.L * p.n_kv_heads;
     const long long units = rows * (D / 16);
     hipLaunchKernelGGL(rotate_keys_kernel<D>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, a.k,
-                       static_cast<uint16_t*>(p.krot), rows, p.n_kv_heads, p.L, p.G, a);
+                       static_cast<uint16_t*>(p.krot), rows, p.n_kv_heads, p.L, p.kv_cap, p.G, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_kernel<D, kPrerotated>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
