@@ -195,6 +195,38 @@ def main():
                          "traffic_unit": "bytes per decode step (split + reduce kernels)"},
         }
 
+    # Batched decode with one length per sequence: 4 sequences of the Qwen3-8B heads, lengths
+    # 16K, 48K, 98512 and 128K in one call (each with its own G), caches of capacity 128K.
+    varlen = None
+    if do_decode:
+        vl = [16384, 49152, 98512, 131072]
+        vcap = 131072
+        gen = torch.Generator(device=dev).manual_seed(6)
+        vk = torch.randn((len(vl), vcap, dcfg.n_kv_heads, dcfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        vv = torch.randn((len(vl), vcap, dcfg.n_kv_heads, dcfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        vq = torch.randn((len(vl), dcfg.n_q_heads, dcfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        vo = torch.empty_like(vq)
+        vlen = torch.tensor(vl, dtype=torch.int32, device=dev)
+        vws_b = Z.bifocal_decode_varlen_workspace_bytes(len(vl), dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, vcap)
+        vws = torch.empty(vws_b, dtype=torch.uint8, device=dev)
+        def vcall():
+            Z.bifocal_decode_varlen(vq, vk, vv, vo, None, len(vl), dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
+                                    vlen, vcap, vcap, dcfg.w0, dcfg.w_pretrained, dcfg.rope_theta, vws, vws_b, sptr)
+        vcall()
+        vev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+        vev[0].record(stream)
+        for i in range(20):
+            vcall()
+            vev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        vms = float(np.median([vev[i].elapsed_time(vev[i + 1]) for i in range(20)]))
+        vbytes = 4096.0 * sum(vl)
+        varlen = {"what": f"one call, {len(vl)} sequences of lengths {vl} (G per sequence), Qwen3-8B heads",
+                  "us_per_call": round(vms * 1e3, 2), "GB/s": round(vbytes / (vms * 1e-3) / 1e9, 1),
+                  "bytes_per_call": vbytes}
+        decode["batched_varlen"] = varlen
+        del vk, vv, vq, vo, vws
+
     if not do_prefill:
         if args.copy_calibration:
             copy_calibration(torch, dev)
@@ -222,6 +254,27 @@ def main():
     fev[2].record(stream)
     torch.cuda.synchronize()
     fused_ms = (fev[0].elapsed_time(fev[1]) + fev[1].elapsed_time(fev[2])) / 2.0
+
+    # Chunked prefill: the last 4096 query rows against the 128K cache (keys 0 .. L-1 already in
+    # it), G from L, keys rotated into the workspace first (as the headline mode).
+    cq0, cql = pcfg.L - 4096, 4096
+    qc = q[:, cq0:].contiguous()
+    oc = torch.empty_like(qc)
+    cflops = 4.0 * pcfg.n_q_heads * pcfg.head_dim * sum(range(cq0 + 1, pcfg.L + 1))
+    def chunk():
+        Z.bifocal_prefill_chunk(qc, k, v, oc, None, pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim, cql,
+                                cq0, pcfg.L, pcfg.w0, pcfg.w_pretrained, pcfg.rope_theta, pws, pws_bytes, sptr)
+    chunk()
+    chev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in chev:
+        e.record(stream)
+        chunk()
+    end = torch.cuda.Event(enable_timing=True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    chev.append(end)
+    chunk_ms = float(np.median([chev[i].elapsed_time(chev[i + 1]) for i in range(6)]))
+    del qc, oc
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -259,6 +312,9 @@ def main():
         "matched_control": {"what": "same kernel, w0 >= L (plain causal RoPE attention)",
                             "ms": round(ctrl_ms, 3), "TFLOP/s": round(ctrl_tflops, 2),
                             "bifocal_over_control": round(ctrl_ms / pre_avg, 4)},
+        "chunked_prefill": {"what": f"rows {cq0}..{pcfg.L - 1} (4096 queries) against the 128K cache, G from L",
+                            "ms": round(chunk_ms, 3), "TFLOP/s": round(cflops / (chunk_ms * 1e-3) / 1e12, 2),
+                            "flops": cflops},
         "decode": decode,
         "cpu_baseline": cpu,
     }

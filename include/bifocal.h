@@ -131,6 +131,29 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
                    int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
                    double rope_theta, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace bifocal_decode_varlen needs for lengths <= max_len with these shapes.
+ * Returns 0 for invalid arguments. */
+size_t bifocal_decode_varlen_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                             int64_t max_len);
+
+/* Batched decode with one length per sequence (a variable-length batch): sequence b's query, at
+ * position L_b - 1, attends its cached keys 0 .. L_b - 1 with its own group size
+ * G_b = max(1, ceil(L_b / w_pretrained)) (review page, Method: G follows the current length).
+ *   seq_lens  [batch] int32 DEVICE array of the lengths L_b; values outside [1, max_len] are
+ *             clamped into it
+ *   max_len   host-side upper bound of every L_b: sizes the split grid and the workspace;
+ *             1 <= max_len <= cache_capacity
+ *   q, k_cache, v_cache, o, lse, w0, w_pretrained, rope_theta, stream: as bifocal_decode;
+ *   workspace >= bifocal_decode_varlen_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+ *             max_len) (each sequence is split into key chunks as if it were decoded alone).
+ * Sequence b's output equals bifocal_decode of that sequence alone at L = L_b.
+ * Returns BIFOCAL_OK or a negative bifocal_status (BIFOCAL_EINVAL when seq_lens is NULL). */
+int bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                          int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                          const int32_t* seq_lens, int64_t max_len, int64_t cache_capacity,
+                          int64_t w0, int64_t w_pretrained, double rope_theta,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Parity hook for the position arithmetic: writes G (from L and w_pretrained) to
  * G_out[0] and f(x) = floor(x / G) to f_out[x] for x < L, using the same device code the
  * attention kernels use (gist.science summary, Methodologie section 1).

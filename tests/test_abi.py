@@ -129,6 +129,36 @@ def test_decode_rejects_before_any_hip_call(lib, kw, expect):
     assert decode_call(lib, **kw) == expect
 
 
+def varlen_call(lib, **kw):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, batch=3, hq=8, hkv=2, d=128, lens=FAKE, max_len=100,
+                cap=128, w0=16, wp=32, theta=1e4, ws=FAKE, wsb=1 << 40)
+    args.update(kw)
+    return lib.bifocal_decode_varlen(args["q"], args["kc"], args["vc"], args["o"], args["lse"], args["batch"],
+                                     args["hq"], args["hkv"], args["d"], args["lens"], args["max_len"], args["cap"],
+                                     args["w0"], args["wp"], args["theta"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(lens=None), EINVAL), (dict(q=None), EINVAL), (dict(max_len=0), EINVAL), (dict(max_len=129), EINVAL),
+    (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL), (dict(theta=-2.0), EINVAL), (dict(batch=0), EINVAL),
+    (dict(d=80), EUNSUP), (dict(hq=16, hkv=2), EUNSUP), (dict(ws=None), EWS), (dict(wsb=16), EWS),
+])
+def test_decode_varlen_rejects_before_any_hip_call(lib, kw, expect):
+    assert varlen_call(lib, **kw) == expect
+
+
+def test_decode_varlen_workspace_query(lib):
+    assert lib.bifocal_decode_varlen_workspace_bytes(0, 8, 2, 128, 100) == 0
+    prev = 0
+    for L in [1, 33, 4096, 98001, 131072]:
+        n = lib.bifocal_decode_varlen_workspace_bytes(3, 32, 8, 128, L)
+        assert n >= prev and n % (3 * 32 * 130 * 4) == 0
+        assert n >= lib.bifocal_decode_workspace_bytes(3, 32, 8, 128, L)
+        prev = n
+    need = lib.bifocal_decode_varlen_workspace_bytes(3, 8, 2, 128, 100)
+    assert varlen_call(lib, wsb=need - 1) == EWS
+
+
 def test_decode_workspace_query(lib):
     assert lib.bifocal_decode_workspace_bytes(0, 8, 2, 128, 100) == 0
     assert lib.bifocal_decode_workspace_bytes(1, 8, 3, 128, 100) == 0

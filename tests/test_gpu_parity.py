@@ -339,6 +339,85 @@ def test_decode_qwen3_8b_across_group_flip():
         assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= LSE_ABS
 
 
+SMALL_VARLEN = [
+    # (cap, Hq, Hkv, D, w_pretrained, w0, theta, per-sequence lengths)
+    (1200, 4, 1, 128, 256, 100, 1e6, [1, 2, 100, 511, 512, 513, 1025, 1200]),  # G from 1 to 5 in one batch
+    (700, 8, 2, 64, 64, 17, 1e4, [700, 33, 64]),
+    (3000, 32, 8, 128, 1000, 128, 1e6, [2000, 3000, 1001, 129]),               # Qwen3-8B heads
+    (500, 4, 4, 128, 100, 0, 1e4, [450, 101, 7]),                                # all remote
+]
+
+
+def run_decode_varlen(q_bits, k_bits, v_bits, lens, max_len, w0, wp, theta):
+    q, kc, vc = dev(q_bits), dev(k_bits), dev(v_bits)
+    B, Hq, D = q.shape
+    obuf, o = guarded((B, Hq, D), torch.bfloat16)
+    lbuf, lse = guarded((B, Hq), torch.float32)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    Z.decode_varlen(q, kc, vc, lens_t, max_len=max_len, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert_guard(obuf, o.numel())
+    assert_guard(lbuf, lse.numel())
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", SMALL_VARLEN, ids=[f"cap{c[0]}H{c[1]}-{c[2]}D{c[3]}w{c[5]}B{len(c[7])}" for c in SMALL_VARLEN])
+def test_decode_varlen_small(case):
+    cap, Hq, Hkv, D, wp, w0, theta, lens = case
+    B = len(lens)
+    say(f"decode varlen {case[:7]} lens={lens}")
+    rng = np.random.default_rng(cap + B)
+    kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    qb = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    o, lse = run_decode_varlen(qb, kb, vb, lens, max(lens), w0, wp, theta)
+    for b, L in enumerate(lens):
+        ref_o, ref_lse = bifocal_decode(f64(qb[b:b + 1]), f64(kb[b:b + 1]), f64(vb[b:b + 1]), L=L, w0=w0,
+                                        w_pretrained=wp, theta=theta)
+        compare(o[b:b + 1], ref_o, f"o seq {b} L={L}")
+        assert np.max(np.abs(lse[b:b + 1] - ref_lse)) <= LSE_ABS
+
+
+def test_decode_varlen_equal_lengths_is_decode():
+    B, cap, Hq, Hkv, D, wp, w0, theta, L = 3, 900, 8, 2, 128, 200, 60, 1e6, 777
+    rng = np.random.default_rng(12)
+    kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    qb = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    o_u, lse_u = run_decode(qb, kb, vb, L, w0, wp, theta)
+    o_v, lse_v = run_decode_varlen(qb, kb, vb, [L] * B, L, w0, wp, theta)
+    assert np.array_equal(o_u, o_v) and np.array_equal(lse_u, lse_v)
+
+
+def test_decode_varlen_clamps_lengths():
+    B, cap, Hq, Hkv, D, wp, w0, theta = 3, 600, 4, 1, 64, 100, 20, 1e4
+    rng = np.random.default_rng(13)
+    kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    qb = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    o_a, lse_a = run_decode_varlen(qb, kb, vb, [0, 500, 9999], 500, w0, wp, theta)
+    o_b, lse_b = run_decode_varlen(qb, kb, vb, [1, 500, 500], 500, w0, wp, theta)
+    assert np.array_equal(o_a, o_b) and np.array_equal(lse_a, lse_b)
+
+
+def test_decode_varlen_qwen3_8b_mixed_lengths():
+    cap, Hq, Hkv, D, wp, w0, theta = 131072, 32, 8, 128, 32768, 2048, 1e6
+    lens = [98305, 131072, 40000]  # G = 4, 4, 2
+    B = len(lens)
+    say(f"decode varlen Qwen3-8B heads, lens={lens}")
+    rng = np.random.default_rng(14)
+    kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    qb = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    o, lse = run_decode_varlen(qb, kb, vb, lens, cap, w0, wp, theta)
+    for b, L in enumerate(lens):
+        ref_o, ref_lse = bifocal_decode(W.bf16_bits_to_float32(qb[b:b + 1]), W.bf16_bits_to_float32(kb[b:b + 1, :L]),
+                                        W.bf16_bits_to_float32(vb[b:b + 1, :L]), L=L, w0=w0, w_pretrained=wp,
+                                        theta=theta)
+        compare(o[b:b + 1], ref_o, f"o seq {b} L={L}")
+        assert np.max(np.abs(lse[b:b + 1] - ref_lse)) <= LSE_ABS
+
+
 def test_decode_matches_prefill_last_row_on_gpu():
     B, L, Hq, Hkv, D, wp, w0, theta = 1, 700, 8, 2, 128, 200, 60, 1e6
     bits = W.random_case(77, B, L, Hq, Hkv, D)

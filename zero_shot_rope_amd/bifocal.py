@@ -24,6 +24,8 @@ EXPORTED_SYMBOLS = (
     "bifocal_prefill_chunk",
     "bifocal_decode_workspace_bytes",
     "bifocal_decode",
+    "bifocal_decode_varlen_workspace_bytes",
+    "bifocal_decode_varlen",
     "bifocal_positions",
     "bifocal_status_string",
 )
@@ -67,6 +69,11 @@ def load_library():
         lib.bifocal_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
                                        c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
         lib.bifocal_decode.restype = c_int
+        lib.bifocal_decode_varlen_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_i64]
+        lib.bifocal_decode_varlen_workspace_bytes.restype = c_sz
+        lib.bifocal_decode_varlen.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
+                                              c_vp, c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
+        lib.bifocal_decode_varlen.restype = c_int
         lib.bifocal_positions.argtypes = [c_i64, c_i64, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32), c_vp]
         lib.bifocal_positions.restype = c_int
@@ -93,6 +100,12 @@ def bifocal_prefill_workspace_bytes(batch: int, n_kv_heads: int, head_dim: int, 
 
 def bifocal_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, max_L: int) -> int:
     return int(load_library().bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, int(max_L)))
+
+
+def bifocal_decode_varlen_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                                          max_len: int) -> int:
+    return int(load_library().bifocal_decode_varlen_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+                                                                    int(max_len)))
 
 
 def _ptr(t) -> Optional[int]:
@@ -148,6 +161,18 @@ def bifocal_decode(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, he
                             float(rope_theta), _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != 0:
         raise BifocalError(st, "bifocal_decode")
+
+
+def bifocal_decode_varlen(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, seq_lens, max_len,
+                          cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes,
+                          stream=None) -> None:
+    lib = load_library()
+    st = lib.bifocal_decode_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _fptr(lse), batch, n_q_heads,
+                                   n_kv_heads, head_dim, _ptr(seq_lens), int(max_len), int(cache_capacity), int(w0),
+                                   int(w_pretrained), float(rope_theta), _ptr(workspace), int(workspace_bytes),
+                                   _stream(stream))
+    if st != 0:
+        raise BifocalError(st, "bifocal_decode_varlen")
 
 
 def bifocal_positions(L, w_pretrained, f_out, G_out, stream=None) -> None:
@@ -250,6 +275,34 @@ def decode(q, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, rope_thet
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     bifocal_decode(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained, rope_theta,
                    workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def decode_varlen(q, k_cache, v_cache, seq_lens, *, max_len: int, w0: int, w_pretrained: int, rope_theta: float,
+                  workspace=None, out=None, lse=None, want_lse: bool = False, stream=None):
+    """q [B, Hq, D]; caches [B, Lcap, Hkv, D]; seq_lens int32 [B] on the device (each <= max_len)
+    -> o [B, Hq, D] (and lse [B, Hq]); sequence b decodes at its own length seq_lens[b]."""
+    import torch
+
+    _check(q, "q", 3)
+    _check(k_cache, "k_cache", 4)
+    _check(v_cache, "v_cache", 4)
+    if not isinstance(seq_lens, torch.Tensor) or seq_lens.dtype != torch.int32 or not seq_lens.is_cuda \
+            or not seq_lens.is_contiguous() or seq_lens.shape != (q.shape[0],):
+        raise ValueError("seq_lens must be a contiguous int32 CUDA/HIP tensor of shape [batch]")
+    B, Hq, D = q.shape
+    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shapes do not match q")
+    need = bifocal_decode_varlen_workspace_bytes(B, Hq, Hkv, D, max_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    bifocal_decode_varlen(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, seq_lens, max_len, cap, w0, w_pretrained,
+                          rope_theta, workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     return (out, lse) if (want_lse or lse is not None) else out
 
 

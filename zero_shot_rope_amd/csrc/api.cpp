@@ -144,10 +144,20 @@ size_t bifocal_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, 
   return static_cast<size_t>(batch) * n_q_heads * s.max_splits * (head_dim + 2) * sizeof(float);
 }
 
-int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                   int batch, int n_q_heads, int n_kv_heads, int head_dim,
-                   int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
-                   double rope_theta, void* workspace, size_t workspace_bytes, void* stream) {
+size_t bifocal_decode_varlen_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                             int64_t max_len) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1 || max_len < 1) return 0;
+  if (max_len > kMaxL || n_q_heads % n_kv_heads != 0) return 0;
+  const bifocal::DecodeSplit s = bifocal::decode_split(max_len, 1, n_kv_heads);
+  return static_cast<size_t>(batch) * n_q_heads * s.max_splits * (head_dim + 2) * sizeof(float);
+}
+
+// Shared by the single-length and the per-sequence-length decode. lens == NULL: every sequence has
+// length L; else lens is a device array and L the maximum length. Checks the shared arguments.
+static int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int batch,
+                       int n_q_heads, int n_kv_heads, int head_dim, const int32_t* lens, int64_t L,
+                       int64_t cache_capacity, int64_t w0, int64_t w_pretrained, double rope_theta, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !o) return BIFOCAL_EINVAL;
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
   if (L < 1 || cache_capacity < L || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta))
@@ -157,13 +167,18 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
   const int group = n_q_heads / n_kv_heads;
   if (group != 1 && group != 2 && group != 4) return BIFOCAL_EUNSUPPORTED;
   if (cache_capacity > kMaxL || batch > 65535) return BIFOCAL_EUNSUPPORTED;  // grid z limit
-  const size_t need = bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L);
+  if (lens != nullptr && (long long)batch * bifocal::decode_split(L, 1, n_kv_heads).max_splits > 0x7fffffffLL)
+    return BIFOCAL_EUNSUPPORTED;  // grid x limit of the interleaved per-sequence grid
+  const size_t need = lens ? bifocal_decode_varlen_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L)
+                           : bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L);
   if (!workspace || workspace_bytes < need) return BIFOCAL_EWORKSPACE;
 
   const int64_t G = bifocal_group_size(L, w_pretrained);
   uint32_t W[64];
   phase_increments(head_dim, rope_theta, W);
-  const bifocal::DecodeSplit s = bifocal::decode_split(L, batch, n_kv_heads);
+  // One length: the batch shares one grid of about one workgroup per CU. Per-sequence lengths:
+  // each sequence is split as if it were alone (its chunks exist up to its own length).
+  const bifocal::DecodeSplit s = bifocal::decode_split(L, lens ? 1 : batch, n_kv_heads);
   bifocal::DecodeLaunch p;
   p.q = q;
   p.k_cache = k_cache;
@@ -171,19 +186,40 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
   p.o = o;
   p.lse = lse;
   p.workspace = static_cast<float*>(workspace);
+  p.lens = lens;
   p.batch = batch;
   p.n_q_heads = n_q_heads;
   p.n_kv_heads = n_kv_heads;
   p.head_dim = head_dim;
   p.L = static_cast<int>(L);
   p.capacity = static_cast<int>(cache_capacity);
-  p.w0 = (G == 1 || w0 >= L) ? static_cast<int>(L) : static_cast<int>(w0);
+  if (lens == nullptr) p.w0 = (G == 1 || w0 >= L) ? static_cast<int>(L) : static_cast<int>(w0);
+  else p.w0 = static_cast<int>(w0 < L ? w0 : L);  // clamped per sequence on the device
   p.G = static_cast<int>(G);
+  p.w_pretrained = static_cast<int>(w_pretrained < (1LL << 30) ? w_pretrained : (1LL << 30));
   p.n_splits = s.n_splits;
   p.chunk = s.chunk;
   p.scale_log2 = scale_log2_for(head_dim);
   p.W = W;
   return map_hip(bifocal::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                   int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                   int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
+                   double rope_theta, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, nullptr, L,
+                     cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream);
+}
+
+int bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                          int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                          const int32_t* seq_lens, int64_t max_len, int64_t cache_capacity,
+                          int64_t w0, int64_t w_pretrained, double rope_theta,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!seq_lens) return BIFOCAL_EINVAL;
+  return decode_impl(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, seq_lens, max_len,
+                     cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream);
 }
 
 int bifocal_positions(int64_t L, int64_t w_pretrained, int32_t* f_out, int32_t* G_out, void* stream) {

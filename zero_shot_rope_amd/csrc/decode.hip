@@ -24,8 +24,11 @@ struct DecodeArgs {
   const uint16_t* kc;
   const uint16_t* vc;
   float* ws;
-  int Hq, Hkv, L, cap;
-  int w0, G;
+  const int32_t* lens;  // per-sequence lengths (device), or NULL: every sequence has length L
+  int B;
+  int Hq, Hkv, L, cap;  // L: the length, or with lens the maximum length
+  int w0, G;            // with lens: w0 as requested, G unused (per sequence from wp)
+  int wp;
   int n_splits, chunk;
   float scale_log2;
   uint32_t W[D / 2];
@@ -78,12 +81,39 @@ void decode_split_kernel(const DecodeArgs<D> a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;  // MFMA 16x16 lane = li + 16 * lg
-  const int split = blockIdx.x, b = blockIdx.z;
+  // One length: grid (split, KV-head group, batch). Per-sequence lengths: the sequences are
+  // interleaved along x (b = x % batch, split = x / batch) so long and short sequences' chunks mix
+  // in the dispatch order.
+  const int split = a.lens ? (int)blockIdx.x / a.B : (int)blockIdx.x;
+  const int b = a.lens ? (int)blockIdx.x % a.B : (int)blockIdx.z;
   const int g = blockIdx.y * kDecWaves + wave;  // KV head of this wave
   const bool head_live = g < a.Hkv;
   const int gl = head_live ? g : 0;
   const int Hg = a.Hq / a.Hkv;
-  const int L = a.L, p = L - 1, w0 = a.w0, G = a.G;
+  // This sequence's length, group size and window: the launch's, or from its own length (lengths
+  // clamped to [1, maximum length]; G = max(1, ceil(L / w_pretrained)); w0 := L when G = 1 or
+  // w0 >= L, as the host does for a single length).
+  int L = a.L, G = a.G, w0 = a.w0;
+  if (a.lens != nullptr) {
+    L = min(max(a.lens[b], 1), a.L);
+    G = (L - 1) / a.wp + 1;
+    if (G == 1 || w0 >= L) w0 = L;
+  }
+  const int p = L - 1;
+  // A chunk past this sequence's end holds no key: its partial is empty (max -inf, sum 0, O 0).
+  if (split * a.chunk >= L) {
+    if (head_live && li < Hg) {
+      float* dst = a.ws + (((size_t)b * a.Hq + (size_t)g * Hg + li) * a.n_splits + split) * (D + 2);
+      if (lg == 0) {
+        dst[0] = kNegBig;
+        dst[1] = 0.f;
+      }
+      for (int d = 4 * lg; d < D; d += 16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[2 + d + r] = 0.f;
+    }
+    return;
+  }
 
   // Query operands (B of S^T = K Q^T): column li = query head g*Hg + li (zero if li >= Hg), rows
   // d = 32c + 8lg .. +8, scaled into log2 units: qs = q~ for local keys, qr = R(Delta_p) q~ for
@@ -442,6 +472,8 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
   a.kc = static_cast<const uint16_t*>(p.k_cache);
   a.vc = static_cast<const uint16_t*>(p.v_cache);
   a.ws = p.workspace;
+  a.lens = p.lens;
+  a.wp = p.w_pretrained;
   a.Hq = p.n_q_heads;
   a.Hkv = p.n_kv_heads;
   a.L = p.L;
@@ -452,8 +484,10 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
   a.chunk = p.chunk;
   a.scale_log2 = p.scale_log2;
   for (int i = 0; i < D / 2; ++i) a.W[i] = p.W[i];
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(p.n_splits, (p.n_kv_heads + kDecWaves - 1) / kDecWaves, p.batch),
-                     dim3(kDecThreads), 0, stream, a);
+  a.B = p.batch;
+  const unsigned groups = (p.n_kv_heads + kDecWaves - 1) / kDecWaves;
+  const dim3 grid = p.lens ? dim3(p.n_splits * p.batch, groups, 1) : dim3(p.n_splits, groups, p.batch);
+  hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(kDecThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, D / 32, p.batch), dim3(kRedThreads), 0, stream,

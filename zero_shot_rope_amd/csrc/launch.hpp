@@ -31,10 +31,12 @@ struct DecodeLaunch {
   void* o;
   float* lse;
   float* workspace;
+  const int32_t* lens;  // per-sequence lengths on the device, or NULL (every sequence has length L)
   int batch, n_q_heads, n_kv_heads, head_dim;
-  int L, capacity;
-  int w0;  // clamped to [0, L]
+  int L, capacity;  // with lens: L is the maximum length
+  int w0;  // clamped to [0, L] (with lens: as requested; clamped per sequence on the device)
   int G;
+  int w_pretrained;
   int n_splits, chunk;
   float scale_log2;
   const uint32_t* W;
