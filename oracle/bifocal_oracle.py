@@ -53,6 +53,7 @@ __all__ = [
     "bifocal_decode",
     "three_pass_attention",
     "raw_bifocal_attention",
+    "decode_step_from_raw",
 ]
 
 
@@ -319,3 +320,29 @@ def raw_bifocal_attention(q_raw, k_raw, v, *, w0: int, w_pretrained: int, theta:
             out[b, :, h] = (e @ v[b, :, kv]) / l
             lse[b, h] = (m + np.log(l))[:, 0]
     return out, lse
+
+
+# ---------------------------------------------------------------------------------------
+# Decode step on the new token's raw vectors ([review] Method: keys are cached at their base
+# positions; [gist] section 2: the cache is never rewritten when G changes)
+# ---------------------------------------------------------------------------------------
+def decode_step_from_raw(q_raw, k_raw, v_new, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int,
+                         theta: float):
+    """The new token sits at position p = L - 1: its raw query and key get base RoPE at p
+    (angle p * omega_k), the rotated key and the value enter the cache at row p, and the step
+    is then `bifocal_decode` at length L.
+
+    q_raw [B, Hq, D]; k_raw, v_new [B, Hkv, D]; caches [B, Lcap, Hkv, D] (rows < p used).
+    Returns (o, lse, k_cache', v_cache') with the updated caches as new float64 arrays.
+    """
+    q_raw = np.asarray(q_raw, dtype=np.float64)
+    k_raw = np.asarray(k_raw, dtype=np.float64)
+    D = q_raw.shape[-1]
+    p = L - 1
+    angles = p * rope_frequencies(D, theta)
+    kc = np.array(k_cache, dtype=np.float64)
+    vc = np.array(v_cache, dtype=np.float64)
+    kc[:, p] = rotate_pairs(k_raw, angles)
+    vc[:, p] = np.asarray(v_new, dtype=np.float64)
+    o, lse = bifocal_decode(rotate_pairs(q_raw, angles), kc, vc, L=L, w0=w0, w_pretrained=w_pretrained, theta=theta)
+    return o, lse, kc, vc

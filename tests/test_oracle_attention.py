@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (bifocal_attention, bifocal_decode, group_size, raw_bifocal_attention,
+from oracle import (bifocal_attention, bifocal_decode, decode_step_from_raw, group_size, raw_bifocal_attention,
                     rope_frequencies, rotate_pairs, three_pass_attention)
 
 
@@ -250,3 +250,28 @@ def test_decode_matches_brute_force():
     o, lse = bifocal_decode(q[:, L - 1], k, v, L=L, w0=w0, w_pretrained=wp, theta=theta)
     np.testing.assert_allclose(o, want[:, L - 1], rtol=0, atol=1e-11)
     np.testing.assert_allclose(lse, want_lse[:, :, L - 1], rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("case", BRUTE_CASES)
+def test_decode_step_from_raw_is_last_row_of_brute_force(case):
+    # The cache holds keys 0 .. p-1 at their base positions (complex rotation) plus garbage at
+    # row p and beyond; the step itself must rotate the new raw key and query at p and append.
+    L, D, Hq, Hkv, wp, w0, theta = case
+    qr, kr, v = _rand(40 + L, 2, L, Hq, Hkv, D)
+    p = L - 1
+    want_o, want_lse = brute_force(qr, kr, v, w0, wp, theta)
+    cap = L + 3
+    rng = np.random.default_rng(L)
+    kc = rng.standard_normal((2, cap, Hkv, D))
+    vc = rng.standard_normal((2, cap, Hkv, D))
+    kc[:, :p] = rope_complex(kr[:, :p], np.arange(p), theta)
+    vc[:, :p] = v[:, :p]
+    o, lse, kc2, vc2 = decode_step_from_raw(qr[:, p], kr[:, p], v[:, p], kc, vc, L=L, w0=w0, w_pretrained=wp,
+                                            theta=theta)
+    np.testing.assert_allclose(o, want_o[:, p], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(lse, want_lse[:, :, p], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(kc2[:, p], rope_complex(kr[:, p:L], [p], theta)[:, 0], rtol=0, atol=1e-12)
+    assert np.array_equal(vc2[:, p], v[:, p])
+    # Rows other than p are untouched, and the inputs are not modified in place.
+    keep = [r for r in range(cap) if r != p]
+    assert np.array_equal(kc2[:, keep], kc[:, keep]) and np.array_equal(vc2[:, keep], vc[:, keep])

@@ -29,6 +29,9 @@ MUTATIONS = [
     ("GQA mapping", "kv = h // group\n                s_base", "kv = h % Hkv\n                s_base"),
     ("lse drops the max", "lse[b, h, start:start + r.size] = (m + np.log(l))[:, 0]",
      "lse[b, h, start:start + r.size] = np.log(l)[:, 0]"),
+    ("new token rotated at L", "angles = p * rope_frequencies(D, theta)", "angles = L * rope_frequencies(D, theta)"),
+    ("new value not appended", "vc[:, p] = np.asarray(v_new, dtype=np.float64)", "vc[:, p] = vc[:, p]"),
+    ("new query left raw", "bifocal_decode(rotate_pairs(q_raw, angles), kc", "bifocal_decode(q_raw, kc"),
 ]
 
 
@@ -56,6 +59,18 @@ def _pins_pass(m) -> bool:
             o, lse = m.bifocal_attention(q, k, v, w0=w0, w_pretrained=wp, theta=theta)
             if not (np.allclose(o, want_o, atol=1e-9, rtol=0) and np.allclose(lse, want_lse, atol=1e-9, rtol=0)):
                 return False
+        # Decode step on raw new-token vectors against the last brute-force row.
+        L, D, Hq, Hkv, wp, w0, theta = 29, 8, 4, 2, 8, 5, 1e4
+        qr, kr, v = _rand(70, 1, L, Hq, Hkv, D)
+        want_o, _ = brute_force(qr, kr, v, w0, wp, theta)
+        kc = rope_complex(kr, np.arange(L), theta)
+        kc[:, L - 1] = 0.0
+        vc = v.copy()
+        vc[:, L - 1] = 0.0
+        o, _, _, _ = m.decode_step_from_raw(qr[:, L - 1], kr[:, L - 1], v[:, L - 1], kc, vc, L=L, w0=w0,
+                                            w_pretrained=wp, theta=theta)
+        if not np.allclose(o, want_o[:, L - 1], atol=1e-9, rtol=0):
+            return False
         # G = 1 against library causal attention.
         q, k, v = _rand(60, 1, 40, 4, 2, 16)
         o, _ = m.bifocal_attention(q, k, v, w0=8, w_pretrained=64, theta=1e4)
