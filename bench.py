@@ -227,6 +227,35 @@ def main():
         decode["batched_varlen"] = varlen
         del vk, vv, vq, vo, vws
 
+    # The same 512 steps taking in each new token raw: base RoPE of its query and key at p = L - 1,
+    # key and value written into cache row p, then the decode (two launches per step).
+    if do_decode:
+        gen = torch.Generator(device=dev).manual_seed(7)
+        nk = torch.randn((dcfg.steps, dcfg.batch, dcfg.n_kv_heads, dcfg.head_dim), generator=gen,
+                         device=dev).to(torch.bfloat16)
+        nv = torch.randn((dcfg.steps, dcfg.batch, dcfg.n_kv_heads, dcfg.head_dim), generator=gen,
+                         device=dev).to(torch.bfloat16)
+        def step_calls():
+            for t in range(dcfg.steps):
+                Z.bifocal_decode_step(qs[t], nk[t], nv[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads,
+                                      dcfg.n_kv_heads, dcfg.head_dim, dcfg.L_first + t, dcfg.capacity, dcfg.w0,
+                                      dcfg.w_pretrained, dcfg.rope_theta, ws, ws_bytes, sptr)
+        step_calls()
+        sev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for i in range(3):
+            sev[i].record(stream)
+            step_calls()
+        sev[3].record(stream)
+        torch.cuda.synchronize()
+        s_ms = float(np.median([sev[i].elapsed_time(sev[i + 1]) for i in range(3)]))
+        sbytes = total_bytes + dcfg.steps * dcfg.batch * (2 * dcfg.n_kv_heads + dcfg.n_q_heads) * dcfg.head_dim * 2
+        decode["step_from_raw"] = {
+            "what": "512 steps, each new token raw: base RoPE of q and k at p, K/V rows appended, then the decode",
+            "ms_per_512_steps": round(s_ms, 3), "us_per_step": round(s_ms * 1e3 / dcfg.steps, 2),
+            "GB/s": round(sbytes / (s_ms * 1e-3) / 1e9, 1),
+            "overhead_us_per_step": round((s_ms - dec_avg) * 1e3 / dcfg.steps, 2)}
+        del nk, nv
+
     if not do_prefill:
         if args.copy_calibration:
             copy_calibration(torch, dev)

@@ -131,6 +131,24 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
                    int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
                    double rope_theta, void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step that also takes in the new token (review page, Method: keys are cached at
+ * their base positions and never rewritten; gist.science summary, Methodologie section 2). The
+ * new token sits at p = L - 1; its query and key arrive raw (before any RoPE):
+ *   q_raw    [batch, n_q_heads, head_dim] bf16, read only
+ *   k_raw    [batch, n_kv_heads, head_dim] bf16, read only
+ *   v_new    [batch, n_kv_heads, head_dim] bf16, read only
+ *   k_cache, v_cache: as bifocal_decode, positions 0..L-2 valid; row L-1 is WRITTEN: the key
+ *            rotated by base RoPE at p (angle p * omega_k, half-split pairs) and the value as is
+ *   o, lse, workspace (>= bifocal_decode_workspace_bytes(..., L)), stream: as bifocal_decode.
+ * The output equals bifocal_decode(rope(q_raw, p), caches with row p written, ..., L). The
+ * rotated query is staged in o before the reduce overwrites it, so o must not alias q_raw,
+ * k_raw or v_new. All arguments are checked before anything is written; on an error return
+ * the caches are untouched. Returns BIFOCAL_OK or a negative bifocal_status. */
+int bifocal_decode_step(const void* q_raw, const void* k_raw, const void* v_new, void* k_cache, void* v_cache,
+                        void* o, float* lse, int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                        int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
+                        double rope_theta, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace bifocal_decode_varlen needs for lengths <= max_len with these shapes.
  * Returns 0 for invalid arguments. */
 size_t bifocal_decode_varlen_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,

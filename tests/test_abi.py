@@ -129,6 +129,27 @@ def test_decode_rejects_before_any_hip_call(lib, kw, expect):
     assert decode_call(lib, **kw) == expect
 
 
+def step_call(lib, **kw):
+    args = dict(qr=FAKE, kr=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, batch=1, hq=8, hkv=2, d=128, L=100,
+                cap=128, w0=16, wp=32, theta=1e4, ws=FAKE, wsb=1 << 40)
+    args.update(kw)
+    return lib.bifocal_decode_step(args["qr"], args["kr"], args["vn"], args["kc"], args["vc"], args["o"], args["lse"],
+                                   args["batch"], args["hq"], args["hkv"], args["d"], args["L"], args["cap"],
+                                   args["w0"], args["wp"], args["theta"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(qr=None), EINVAL), (dict(kr=None), EINVAL), (dict(vn=None), EINVAL), (dict(kc=None), EINVAL),
+    (dict(vc=None), EINVAL), (dict(o=None), EINVAL), (dict(L=0), EINVAL), (dict(L=129), EINVAL),
+    (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL), (dict(theta=float("nan")), EINVAL), (dict(hq=6, hkv=4), EINVAL),
+    (dict(d=96), EUNSUP), (dict(hq=16, hkv=2), EUNSUP), (dict(cap=(1 << 30) + 1), EUNSUP), (dict(ws=None), EWS),
+    (dict(wsb=0), EWS),
+])
+def test_decode_step_rejects_before_any_hip_call(lib, kw, expect):
+    # Every rejection happens before the cache row is written (the fake pointers are never touched).
+    assert step_call(lib, **kw) == expect
+
+
 def varlen_call(lib, **kw):
     args = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, batch=3, hq=8, hkv=2, d=128, lens=FAKE, max_len=100,
                 cap=128, w0=16, wp=32, theta=1e4, ws=FAKE, wsb=1 << 40)

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import aliased_positions, bifocal_attention, bifocal_decode, group_size
+from oracle import aliased_positions, bifocal_attention, bifocal_decode, decode_step_from_raw, group_size
 from zero_shot_rope_amd import bifocal as Z
 from zero_shot_rope_amd import workloads as W
 
@@ -337,6 +337,101 @@ def test_decode_qwen3_8b_across_group_flip():
                                         w_pretrained=cfg.w_pretrained, theta=cfg.rope_theta)
         compare(o.float().cpu().numpy(), ref_o, f"o step {t}")
         assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= LSE_ABS
+
+
+def run_decode_step(qr_bits, kr_bits, vn_bits, kc, vc, L, w0, wp, theta):
+    """kc / vc: device caches, updated in place at row L - 1."""
+    qr, kr, vn = dev(qr_bits), dev(kr_bits), dev(vn_bits)
+    B, Hq, D = qr.shape
+    obuf, o = guarded((B, Hq, D), torch.bfloat16)
+    lbuf, lse = guarded((B, Hq), torch.float32)
+    Z.decode_step(qr, kr, vn, kc, vc, L=L, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert_guard(obuf, o.numel())
+    assert_guard(lbuf, lse.numel())
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def bits_of(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_rotated_row(gpu_bits, ref, what):
+    """A key rotated in fp32 and rounded once to bf16: within one bf16 rounding of the exact value
+    (half an ulp, 2^-9 relative) plus the angle's fixed-point error."""
+    got = W.bf16_bits_to_float32(gpu_bits).astype(np.float64)
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-3
+    say(f"  {what}: max_abs={float(err.max()):.3e}")
+    assert np.all(err <= bound), f"{what}: rotated key row off by {float((err - bound).max())} beyond bound"
+
+
+DECODE_STEP = [
+    # (batch, cap, Hq, Hkv, D, w_pretrained, w0, theta, first L, steps)
+    (1, 300, 4, 1, 128, 128, 50, 1e6, 254, 6),    # G flips 2 -> 3 at L = 257
+    (2, 200, 4, 2, 64, 64, 17, 1e4, 1, 4),        # from an empty cache (p = 0)
+    (1, 3000, 32, 8, 128, 1000, 128, 1e6, 2999, 2),  # Qwen3-8B heads, last rows of the cache
+]
+
+
+@pytest.mark.parametrize("case", DECODE_STEP, ids=[f"B{c[0]}cap{c[1]}H{c[2]}-{c[3]}D{c[4]}L{c[8]}" for c in DECODE_STEP])
+def test_decode_step_sequence(case):
+    """Consecutive steps on one cache, each from raw new-token vectors, against the oracle run
+    on its own (float64) cache; the written rows and the untouched rest are checked too."""
+    B, cap, Hq, Hkv, D, wp, w0, theta, L0, steps = case
+    rng = np.random.default_rng(cap + L0)
+    kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    kc, vc = dev(kb), dev(vb)
+    k_ref, v_ref = f64(kb), f64(vb)
+    for t in range(steps):
+        L = L0 + t
+        p = L - 1
+        say(f"decode step {case[:8]} L={L} G={group_size(L, wp)}")
+        qr = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+        kr = W.round_to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+        vn = W.round_to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+        before_k, before_v = bits_of(kc), bits_of(vc)
+        o, lse = run_decode_step(qr, kr, vn, kc, vc, L, w0, wp, theta)
+        ref_o, ref_lse, k_ref, v_ref = decode_step_from_raw(f64(qr), f64(kr), f64(vn), k_ref, v_ref, L=L, w0=w0,
+                                                            w_pretrained=wp, theta=theta)
+        compare(o, ref_o, f"o L={L}")
+        assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
+        after_k, after_v = bits_of(kc), bits_of(vc)
+        check_rotated_row(after_k[:, p], k_ref[:, p], f"key row {p}")
+        assert np.array_equal(after_v[:, p], vn), "value row not appended bit for bit"
+        keep = np.ones(cap, dtype=bool)
+        keep[p] = False
+        assert np.array_equal(after_k[:, keep], before_k[:, keep]), "key rows other than p changed"
+        assert np.array_equal(after_v[:, keep], before_v[:, keep]), "value rows other than p changed"
+        if p == 0:
+            # Zero angle: the key enters unchanged, and one key makes the output its value.
+            assert np.array_equal(after_k[:, 0], kr)
+            group = Hq // Hkv
+            assert np.array_equal(W.round_to_bf16_bits(o.astype(np.float32)), np.repeat(vn, group, axis=1))
+
+
+def test_decode_step_qwen3_8b_full_cache():
+    cfg = W.QWEN3_8B_DECODE
+    say(f"decode step {cfg.name} (full cache, raw new token)")
+    bits = W.decode_inputs(cfg)
+    L = cfg.L_first + 511
+    p = L - 1
+    kc, vc = dev(bits["k_cache"]), dev(bits["v_cache"])
+    rng = np.random.default_rng(98)
+    B, Hq, Hkv, D = 1, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    qr = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    kr = W.round_to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+    vn = W.round_to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+    o, lse = run_decode_step(qr, kr, vn, kc, vc, L, cfg.w0, cfg.w_pretrained, cfg.rope_theta)
+    ref_o, ref_lse, k_ref, _ = decode_step_from_raw(f64(qr), f64(kr), f64(vn), W.bf16_bits_to_float32(bits["k_cache"]),
+                                                    W.bf16_bits_to_float32(bits["v_cache"]), L=L, w0=cfg.w0,
+                                                    w_pretrained=cfg.w_pretrained, theta=cfg.rope_theta)
+    compare(o, ref_o, f"o L={L}")
+    assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
+    row = kc[:, p].cpu().view(torch.int16).numpy().view(np.uint16)
+    check_rotated_row(row, k_ref[:, p], f"key row {p}")
+    assert np.array_equal(vc[:, p].cpu().view(torch.int16).numpy().view(np.uint16), vn)
 
 
 SMALL_VARLEN = [

@@ -24,6 +24,7 @@ EXPORTED_SYMBOLS = (
     "bifocal_prefill_chunk",
     "bifocal_decode_workspace_bytes",
     "bifocal_decode",
+    "bifocal_decode_step",
     "bifocal_decode_varlen_workspace_bytes",
     "bifocal_decode_varlen",
     "bifocal_positions",
@@ -69,6 +70,9 @@ def load_library():
         lib.bifocal_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
                                        c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
         lib.bifocal_decode.restype = c_int
+        lib.bifocal_decode_step.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
+                                            c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
+        lib.bifocal_decode_step.restype = c_int
         lib.bifocal_decode_varlen_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_i64]
         lib.bifocal_decode_varlen_workspace_bytes.restype = c_sz
         lib.bifocal_decode_varlen.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
@@ -161,6 +165,18 @@ def bifocal_decode(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, he
                             float(rope_theta), _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != 0:
         raise BifocalError(st, "bifocal_decode")
+
+
+def bifocal_decode_step(q_raw, k_raw, v_new, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L,
+                        cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes,
+                        stream=None) -> None:
+    lib = load_library()
+    st = lib.bifocal_decode_step(_ptr(q_raw), _ptr(k_raw), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+                                 _fptr(lse), batch, n_q_heads, n_kv_heads, head_dim, int(L), int(cache_capacity),
+                                 int(w0), int(w_pretrained), float(rope_theta), _ptr(workspace), int(workspace_bytes),
+                                 _stream(stream))
+    if st != 0:
+        raise BifocalError(st, "bifocal_decode_step")
 
 
 def bifocal_decode_varlen(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, seq_lens, max_len,
@@ -275,6 +291,37 @@ def decode(q, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, rope_thet
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     bifocal_decode(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained, rope_theta,
                    workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def decode_step(q_raw, k_raw, v_new, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, rope_theta: float,
+                workspace=None, out=None, lse=None, want_lse: bool = False, stream=None):
+    """The new token at p = L - 1 from raw (pre-RoPE) vectors: q_raw [B, Hq, D], k_raw and v_new
+    [B, Hkv, D]. Writes its rotated key and its value into cache row p (in place), then decodes
+    -> o [B, Hq, D] (and lse [B, Hq])."""
+    import torch
+
+    _check(q_raw, "q_raw", 3)
+    _check(k_raw, "k_raw", 3)
+    _check(v_new, "v_new", 3)
+    _check(k_cache, "k_cache", 4)
+    _check(v_cache, "v_cache", 4)
+    B, Hq, D = q_raw.shape
+    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shapes do not match q_raw")
+    if k_raw.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D):
+        raise ValueError("k_raw / v_new must be [batch, n_kv_heads, head_dim]")
+    need = bifocal_decode_workspace_bytes(B, Hq, Hkv, D, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q_raw.device)
+    if out is None:
+        out = torch.empty_like(q_raw)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q_raw.device)
+    bifocal_decode_step(q_raw, k_raw, v_new, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained,
+                        rope_theta, workspace, workspace.numel() * workspace.element_size(),
+                        _stream(stream, q_raw.device))
     return (out, lse) if (want_lse or lse is not None) else out
 
 

@@ -501,6 +501,67 @@ hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// New-token preparation for a decode step on raw (pre-RoPE) vectors: base RoPE at position p
+// (angle p * omega_k, the same exact fixed-point phase as the correction rotation) of the query
+// (into q_out) and of the key (into cache row p), and the value copied into cache row p. One
+// thread per 8 rotation pairs of one head row: the B * Hq query rows, then the B * Hkv key rows.
+template <int D>
+__global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* __restrict__ q_raw,
+                                                          const uint16_t* __restrict__ k_raw,
+                                                          const uint16_t* __restrict__ v_new, uint16_t* __restrict__ q_out,
+                                                          uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int B,
+                                                          int Hq, int Hkv, int p, int cap, const DecodeArgs<D> a) {
+  constexpr int HALF = D / 2, MCH = HALF / 8;
+  const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long nq = (long long)B * Hq * MCH, nk = (long long)B * Hkv * MCH;
+  if (u >= nq + nk) return;
+  const int m = (int)(u % MCH);
+  const uint16_t* src;
+  uint16_t* dst;
+  if (u < nq) {
+    const long long row = u / MCH;  // b * Hq + h
+    src = q_raw + (size_t)row * D;
+    dst = q_out + (size_t)row * D;
+  } else {
+    const long long row = (u - nq) / MCH;  // b * Hkv + g
+    const long long b = row / Hkv, g = row % Hkv;
+    const size_t cache_row = ((size_t)b * cap + p) * Hkv + g;
+    src = k_raw + (size_t)row * D;
+    dst = kc + cache_row * D;
+    const uint16_t* vs = v_new + (size_t)row * D;
+    uint16_t* vd = vc + cache_row * D;
+    *reinterpret_cast<u32x4*>(vd + 8 * m) = *reinterpret_cast<const u32x4*>(vs + 8 * m);
+    *reinterpret_cast<u32x4*>(vd + HALF + 8 * m) = *reinterpret_cast<const u32x4*>(vs + HALF + 8 * m);
+  }
+  u32x4 lo = *reinterpret_cast<const u32x4*>(src + 8 * m);
+  u32x4 hi = *reinterpret_cast<const u32x4*>(src + HALF + 8 * m);
+  uint32_t w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = a.W[8 * m + e];
+  rotate8(lo, hi, p, w);
+  *reinterpret_cast<u32x4*>(dst + 8 * m) = lo;
+  *reinterpret_cast<u32x4*>(dst + HALF + 8 * m) = hi;
+}
+
+template <int D>
+static hipError_t launch_rope_append_d(const RopeAppendLaunch& r, hipStream_t stream) {
+  DecodeArgs<D> a{};
+  for (int i = 0; i < D / 2; ++i) a.W[i] = r.W[i];
+  const long long units = (long long)r.batch * (r.n_q_heads + r.n_kv_heads) * (D / 16);
+  hipLaunchKernelGGL(rope_append_kernel<D>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(r.q_raw), static_cast<const uint16_t*>(r.k_raw),
+                     static_cast<const uint16_t*>(r.v_new), static_cast<uint16_t*>(r.q_out),
+                     static_cast<uint16_t*>(r.k_cache), static_cast<uint16_t*>(r.v_cache), r.batch, r.n_q_heads,
+                     r.n_kv_heads, r.p, r.capacity, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_append(const RopeAppendLaunch& r, hipStream_t stream) {
+  if (r.head_dim == 128) return launch_rope_append_d<128>(r, stream);
+  if (r.head_dim == 64) return launch_rope_append_d<64>(r, stream);
+  return hipErrorInvalidValue;
+}
+
 // Parity hook: G and f(x) from the same device position helpers the attention kernels use.
 __global__ void positions_kernel(int L, int G, int32_t* __restrict__ f_out, int32_t* __restrict__ G_out) {
   const int x = blockIdx.x * blockDim.x + threadIdx.x;

@@ -42,7 +42,21 @@ struct DecodeLaunch {
   const uint32_t* W;
 };
 
+// New token of a decode step: base RoPE at position p into q_out and cache row p, value copied.
+struct RopeAppendLaunch {
+  const void* q_raw;
+  const void* k_raw;
+  const void* v_new;
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+  int batch, n_q_heads, n_kv_heads, head_dim;
+  int p, capacity;
+  const uint32_t* W;
+};
+
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
+hipError_t launch_rope_append(const RopeAppendLaunch& r, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
 size_t prefill_workspace_bytes(long long batch, long long L, int n_kv_heads, int head_dim);
 hipError_t launch_positions(int L, int G, int32_t* f_out, int32_t* G_out, hipStream_t stream);
