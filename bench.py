@@ -256,6 +256,31 @@ def main():
             "overhead_us_per_step": round((s_ms - dec_avg) * 1e3 / dcfg.steps, 2)}
         del nk, nv
 
+    # The unfused three-pass decode (the pages' fusion ablation): per step the whole cache's keys
+    # are rotated into a copy, then three plain decode passes and a merge.
+    if do_decode:
+        uws_b = Z.bifocal_decode_unfused_workspace_bytes(dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
+                                                         dcfg.capacity)
+        uws = torch.empty(uws_b, dtype=torch.uint8, device=dev)
+        def unfused_steps():
+            for t in range(dcfg.steps):
+                Z.bifocal_decode_unfused(qs[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads,
+                                         dcfg.head_dim, dcfg.L_first + t, dcfg.capacity, dcfg.w0, dcfg.w_pretrained,
+                                         dcfg.rope_theta, uws, uws_b, sptr)
+        unfused_steps()
+        uev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for i in range(2):
+            uev[i].record(stream)
+            unfused_steps()
+        uev[2].record(stream)
+        torch.cuda.synchronize()
+        u_ms = float(np.median([uev[i].elapsed_time(uev[i + 1]) for i in range(2)]))
+        decode["unfused_three_pass"] = {
+            "what": "512 steps, each: all cached keys rotated into a copy, three plain decode passes, LSE merge",
+            "ms_per_512_steps": round(u_ms, 3), "us_per_step": round(u_ms * 1e3 / dcfg.steps, 2),
+            "fused_over_unfused_throughput": round(u_ms / dec_avg, 3)}
+        del uws
+
     if not do_prefill:
         if args.copy_calibration:
             copy_calibration(torch, dev)
@@ -305,6 +330,24 @@ def main():
     chunk_ms = float(np.median([chev[i].elapsed_time(chev[i + 1]) for i in range(6)]))
     del qc, oc
 
+    # The unfused three-pass prefill (the pages' fusion ablation): q and k rotated into copies,
+    # three plain attention launches (window/base, causal/remote, window/remote), LSE merge.
+    uws_b = Z.bifocal_prefill_unfused_workspace_bytes(pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim,
+                                                      pcfg.L)
+    uws = torch.empty(uws_b, dtype=torch.uint8, device=dev)
+    def unfused():
+        Z.bifocal_prefill_unfused(q, k, v, o, None, pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim, pcfg.L,
+                                  pcfg.w0, pcfg.w_pretrained, pcfg.rope_theta, uws, uws_b, sptr)
+    unfused()
+    uev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for i in range(2):
+        uev[i].record(stream)
+        unfused()
+    uev[2].record(stream)
+    torch.cuda.synchronize()
+    unfused_ms = float(np.median([uev[i].elapsed_time(uev[i + 1]) for i in range(2)]))
+    del uws
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(pb, pcfg, args.cpu_seconds)
@@ -344,6 +387,10 @@ def main():
         "chunked_prefill": {"what": f"rows {cq0}..{pcfg.L - 1} (4096 queries) against the 128K cache, G from L",
                             "ms": round(chunk_ms, 3), "TFLOP/s": round(cflops / (chunk_ms * 1e-3) / 1e12, 2),
                             "flops": cflops},
+        "unfused_three_pass": {"what": "rotations into copies, three plain attention launches, LSE merge",
+                               "ms": round(unfused_ms, 3), "TFLOP/s": round(flops / (unfused_ms * 1e-3) / 1e12, 2),
+                               "fused_over_unfused_throughput": round(unfused_ms / pre_avg, 3),
+                               "unfused_over_control_throughput": round(ctrl_ms / unfused_ms, 3)},
         "decode": decode,
         "cpu_baseline": cpu,
     }

@@ -172,6 +172,45 @@ int bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cach
                           int64_t w0, int64_t w_pretrained, double rope_theta,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Unfused three-pass forms (an ablation of the fusion, same results) ----
+ * The pages write the prefill as three ordinary attention calls merged by inclusion-exclusion
+ * (review page, Method; gist.science summary, Methodologie section 2): A = sliding window w0 on
+ * the base-position vectors, B = full causal on the remote vectors R(Delta) q, R(Delta) k, C =
+ * sliding window w0 on the remote vectors, then O = (W_A O_A + W_B O_B - W_C O_C) /
+ * (W_A + W_B - W_C), W_X = exp(LSE_X - max(LSE_A, LSE_B)). These entry points run exactly that:
+ * the remote vectors are rotated into the workspace, each pass is a separate plain-attention
+ * launch writing bf16 O_X and fp32 LSE_X to the workspace, and a merge kernel writes o (and lse).
+ * They exist to measure what the fusion saves; the results match the fused calls within bf16
+ * rounding of the intermediate outputs. */
+
+/* Bytes of workspace for bifocal_prefill_unfused; 0 for invalid arguments. */
+size_t bifocal_prefill_unfused_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                               int64_t L);
+
+/* Arguments as bifocal_prefill (q, k, v post-base-RoPE); the workspace is required:
+ * >= bifocal_prefill_unfused_workspace_bytes(...), caller-owned, clobbered. Six to eight
+ * launches on `stream` (two rotations, three passes or one when w0 = 0, one merge).
+ * Returns BIFOCAL_OK or a negative bifocal_status. */
+int bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                            int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace for bifocal_decode_unfused at any L <= cache_capacity; 0 for invalid
+ * arguments. It holds a rotated copy of the whole key cache ([batch, cache_capacity,
+ * n_kv_heads, head_dim] bf16). */
+size_t bifocal_decode_unfused_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                              int64_t cache_capacity);
+
+/* Arguments as bifocal_decode; the workspace must hold
+ * bifocal_decode_unfused_workspace_bytes(..., cache_capacity) bytes. Per call: all L cached
+ * keys are rotated into the workspace copy, then three plain decode passes (each a split and
+ * a reduce launch) and the merge. Returns BIFOCAL_OK or a negative bifocal_status. */
+int bifocal_decode_unfused(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                           int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                           int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
+                           double rope_theta, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Parity hook for the position arithmetic: writes G (from L and w_pretrained) to
  * G_out[0] and f(x) = floor(x / G) to f_out[x] for x < L, using the same device code the
  * attention kernels use (gist.science summary, Methodologie section 1).

@@ -214,3 +214,62 @@ def test_prefill_workspace_query(lib):
     assert lib.bifocal_prefill_workspace_bytes(2, 2, 64, 100) == 2 * 100 * 2 * 64 * 2
     for bad in [(0, 8, 128, 10), (1, 0, 128, 10), (1, 8, 96, 10), (1, 8, 128, 0), (1, 8, 128, (1 << 30) + 1)]:
         assert lib.bifocal_prefill_workspace_bytes(*bad) == 0
+
+
+def prefill_unfused_call(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, batch=1, hq=4, hkv=2, d=128, L=256, w0=32, wp=64,
+                theta=1e4, ws=FAKE, wsb=1 << 40)
+    args.update(kw)
+    return lib.bifocal_prefill_unfused(args["q"], args["k"], args["v"], args["o"], args["lse"], args["batch"],
+                                       args["hq"], args["hkv"], args["d"], args["L"], args["w0"], args["wp"],
+                                       args["theta"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), EINVAL), (dict(k=None), EINVAL), (dict(v=None), EINVAL), (dict(o=None), EINVAL),
+    (dict(batch=0), EINVAL), (dict(L=0), EINVAL), (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL),
+    (dict(theta=0.0), EINVAL), (dict(hq=6, hkv=4), EINVAL), (dict(d=96), EUNSUP), (dict(L=(1 << 30) + 1), EUNSUP),
+    (dict(ws=None), EWS), (dict(wsb=0), EWS),
+])
+def test_prefill_unfused_rejects_before_any_hip_call(lib, kw, expect):
+    assert prefill_unfused_call(lib, **kw) == expect
+
+
+def test_prefill_unfused_workspace_query(lib):
+    assert lib.bifocal_prefill_unfused_workspace_bytes(0, 4, 2, 128, 256) == 0
+    assert lib.bifocal_prefill_unfused_workspace_bytes(1, 4, 2, 96, 256) == 0
+    # q' + k' + three pass outputs (bf16) + three LSEs (fp32), each region 256-byte aligned.
+    B, Hq, Hkv, D, L = 2, 4, 2, 128, 300
+    q, k, lse = B * L * Hq * D * 2, B * L * Hkv * D * 2, B * Hq * L * 4
+    a = lambda x: (x + 255) // 256 * 256
+    assert lib.bifocal_prefill_unfused_workspace_bytes(B, Hq, Hkv, D, L) == 4 * a(q) + a(k) + 3 * a(lse)
+    need = lib.bifocal_prefill_unfused_workspace_bytes(1, 4, 2, 128, 256)
+    assert prefill_unfused_call(lib, wsb=need - 1) == EWS
+
+
+def decode_unfused_call(lib, **kw):
+    args = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, batch=1, hq=8, hkv=2, d=128, L=100, cap=128,
+                w0=16, wp=32, theta=1e4, ws=FAKE, wsb=1 << 40)
+    args.update(kw)
+    return lib.bifocal_decode_unfused(args["q"], args["kc"], args["vc"], args["o"], args["lse"], args["batch"],
+                                      args["hq"], args["hkv"], args["d"], args["L"], args["cap"], args["w0"],
+                                      args["wp"], args["theta"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), EINVAL), (dict(kc=None), EINVAL), (dict(vc=None), EINVAL), (dict(o=None), EINVAL),
+    (dict(L=0), EINVAL), (dict(L=129), EINVAL), (dict(w0=-3), EINVAL), (dict(wp=0), EINVAL),
+    (dict(theta=0.0), EINVAL), (dict(hq=7, hkv=2), EINVAL), (dict(batch=0), EINVAL),
+    (dict(d=80), EUNSUP), (dict(hq=16, hkv=2), EUNSUP), (dict(cap=(1 << 30) + 1), EUNSUP),
+    (dict(ws=None), EWS), (dict(wsb=1024), EWS),
+])
+def test_decode_unfused_rejects_before_any_hip_call(lib, kw, expect):
+    assert decode_unfused_call(lib, **kw) == expect
+
+
+def test_decode_unfused_workspace_query(lib):
+    assert lib.bifocal_decode_unfused_workspace_bytes(0, 8, 2, 128, 128) == 0
+    n = lib.bifocal_decode_unfused_workspace_bytes(1, 8, 2, 128, 128)
+    # At least the rotated key copy plus the split workspace of a plain decode.
+    assert n >= 128 * 2 * 128 * 2 + lib.bifocal_decode_workspace_bytes(1, 8, 2, 128, 128)
+    assert decode_unfused_call(lib, wsb=n - 1) == EWS

@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import aliased_positions, bifocal_attention, bifocal_decode, decode_step_from_raw, group_size
+from oracle import (aliased_positions, bifocal_attention, bifocal_decode, decode_step_from_raw, group_size,
+                    three_pass_attention)
 from zero_shot_rope_amd import bifocal as Z
 from zero_shot_rope_amd import workloads as W
 
@@ -63,17 +64,22 @@ def compare(gpu, ref, what):
 
 def run_prefill(bits, w0, wp, theta, mode="prerotated"):
     """mode "fused": no workspace (keys rotated per tile in the attention kernel);
-    "prerotated": keys rotated once into a (guarded) workspace first."""
+    "prerotated": keys rotated once into a (guarded) workspace first; "unfused": the three-pass
+    form (three plain attention launches and a merge, guarded workspace)."""
     q, k, v = dev(bits["q"]), dev(bits["k"]), dev(bits["v"])
     B, L, Hq, D = q.shape
     obuf, o = guarded((B, L, Hq, D), torch.bfloat16)
     lbuf, lse = guarded((B, Hq, L), torch.float32)
     ws = None
-    if mode == "prerotated":
-        nws = Z.bifocal_prefill_workspace_bytes(B, k.shape[2], D, L)
+    if mode in ("prerotated", "unfused"):
+        nws = (Z.bifocal_prefill_workspace_bytes(B, k.shape[2], D, L) if mode == "prerotated"
+               else Z.bifocal_prefill_unfused_workspace_bytes(B, Hq, k.shape[2], D, L))
         wbuf = torch.full((nws + GUARD,), 0x5A, dtype=torch.uint8, device="cuda")
         ws = wbuf[:nws]
-    Z.prefill(q, k, v, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse, workspace=ws)
+    if mode == "unfused":
+        Z.prefill_unfused(q, k, v, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse, workspace=ws)
+    else:
+        Z.prefill(q, k, v, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     assert_guard(obuf, o.numel())
     assert_guard(lbuf, lse.numel())
@@ -116,14 +122,16 @@ SMALL_PREFILL = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["prerotated", "fused"])
+@pytest.mark.parametrize("mode", ["prerotated", "fused", "unfused"])
 @pytest.mark.parametrize("case", SMALL_PREFILL, ids=[f"B{c[0]}L{c[1]}H{c[2]}-{c[3]}D{c[4]}wp{c[5]}w{c[6]}" for c in SMALL_PREFILL])
 def test_prefill_small(case, mode):
     B, L, Hq, Hkv, D, wp, w0, theta = case
     say(f"prefill small {case} {mode}")
     bits = W.random_case(1000 + L + Hq, B, L, Hq, Hkv, D)
     o, lse = run_prefill(bits, w0, wp, theta, mode)
-    ref_o, ref_lse = bifocal_attention(f64(bits["q"]), f64(bits["k"]), f64(bits["v"]), w0=w0, w_pretrained=wp, theta=theta)
+    # The unfused form is checked against the oracle's own three-pass merge.
+    ref = three_pass_attention if mode == "unfused" else bifocal_attention
+    ref_o, ref_lse = ref(f64(bits["q"]), f64(bits["k"]), f64(bits["v"]), w0=w0, w_pretrained=wp, theta=theta)
     compare(o, ref_o, "o")
     assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
 
@@ -193,7 +201,7 @@ def test_prefill_qwen3_4b_64k(w0):
     full_size_prefill(W.QWEN3_4B_64K[w0], seed=40 + w0)
 
 
-@pytest.mark.parametrize("mode", ["prerotated", "fused"])
+@pytest.mark.parametrize("mode", ["prerotated", "fused", "unfused"])
 def test_prefill_qwen3_8b_128k(mode):
     full_size_prefill(W.QWEN3_8B_128K, seed=41, mode=mode)
 
@@ -276,15 +284,26 @@ def test_prefill_chunk_qwen3_8b_last_4k():
 # ---------------------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------------------
-def run_decode(q_bits, k_bits, v_bits, L, w0, wp, theta, workspace=None):
+def run_decode(q_bits, k_bits, v_bits, L, w0, wp, theta, workspace=None, mode="fused"):
+    """mode "unfused": the three-pass form, with a guarded workspace."""
     q, kc, vc = dev(q_bits), dev(k_bits), dev(v_bits)
     B, Hq, D = q.shape
     obuf, o = guarded((B, Hq, D), torch.bfloat16)
     lbuf, lse = guarded((B, Hq), torch.float32)
-    Z.decode(q, kc, vc, L=L, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse, workspace=workspace)
+    if mode == "unfused":
+        nws = Z.bifocal_decode_unfused_workspace_bytes(B, Hq, kc.shape[2], D, kc.shape[1])
+        wbuf = torch.full((nws + GUARD,), 0x5A, dtype=torch.uint8, device="cuda")
+        Z.decode_unfused(q, kc, vc, L=L, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse,
+                         workspace=wbuf[:nws])
+    else:
+        Z.decode(q, kc, vc, L=L, w0=w0, w_pretrained=wp, rope_theta=theta, out=o, lse=lse, workspace=workspace)
     torch.cuda.synchronize()
     assert_guard(obuf, o.numel())
     assert_guard(lbuf, lse.numel())
+    if mode == "unfused":
+        assert torch.all(wbuf[nws:] == 0x5A), "write outside the workspace"
+        # The cache itself is only read.
+        assert torch.equal(kc, dev(k_bits)) and torch.equal(vc, dev(v_bits))
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
 
@@ -299,16 +318,17 @@ SMALL_DECODE = [
 ]
 
 
+@pytest.mark.parametrize("mode", ["fused", "unfused"])
 @pytest.mark.parametrize("case", SMALL_DECODE, ids=[f"B{c[0]}cap{c[1]}H{c[2]}-{c[3]}D{c[4]}w{c[6]}" for c in SMALL_DECODE])
-def test_decode_small(case):
+def test_decode_small(case, mode):
     B, cap, Hq, Hkv, D, wp, w0, theta, Ls = case
     rng = np.random.default_rng(cap + Hq)
     kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
     vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
     for L in Ls:
-        say(f"decode small {case[:8]} L={L}")
+        say(f"decode small {case[:8]} L={L} {mode}")
         qb = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
-        o, lse = run_decode(qb, kb, vb, L, w0, wp, theta)
+        o, lse = run_decode(qb, kb, vb, L, w0, wp, theta, mode=mode)
         ref_o, ref_lse = bifocal_decode(f64(qb), f64(kb), f64(vb), L=L, w0=w0, w_pretrained=wp, theta=theta)
         compare(o, ref_o, f"o L={L}")
         assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
@@ -432,6 +452,24 @@ def test_decode_step_qwen3_8b_full_cache():
     row = kc[:, p].cpu().view(torch.int16).numpy().view(np.uint16)
     check_rotated_row(row, k_ref[:, p], f"key row {p}")
     assert np.array_equal(vc[:, p].cpu().view(torch.int16).numpy().view(np.uint16), vn)
+
+
+def test_decode_unfused_qwen3_8b():
+    """The three-pass decode on the full 98K cache, on both sides of the change of G."""
+    cfg = W.QWEN3_8B_DECODE
+    say(f"decode unfused {cfg.name} (full cache)")
+    bits = W.decode_inputs(cfg)
+    kf = W.bf16_bits_to_float32(bits["k_cache"])
+    vf = W.bf16_bits_to_float32(bits["v_cache"])
+    for t in [0, 304]:
+        L = cfg.L_first + t
+        say(f"  step {t}: L={L} G={group_size(L, cfg.w_pretrained)}")
+        o, lse = run_decode(bits["q_steps"][t], bits["k_cache"], bits["v_cache"], L, cfg.w0, cfg.w_pretrained,
+                            cfg.rope_theta, mode="unfused")
+        ref_o, ref_lse = bifocal_decode(W.bf16_bits_to_float32(bits["q_steps"][t]), kf, vf, L=L, w0=cfg.w0,
+                                        w_pretrained=cfg.w_pretrained, theta=cfg.rope_theta)
+        compare(o, ref_o, f"o step {t}")
+        assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
 
 
 SMALL_VARLEN = [

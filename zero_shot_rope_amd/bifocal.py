@@ -27,6 +27,10 @@ EXPORTED_SYMBOLS = (
     "bifocal_decode_step",
     "bifocal_decode_varlen_workspace_bytes",
     "bifocal_decode_varlen",
+    "bifocal_prefill_unfused_workspace_bytes",
+    "bifocal_prefill_unfused",
+    "bifocal_decode_unfused_workspace_bytes",
+    "bifocal_decode_unfused",
     "bifocal_positions",
     "bifocal_status_string",
 )
@@ -78,6 +82,16 @@ def load_library():
         lib.bifocal_decode_varlen.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
                                               c_vp, c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
         lib.bifocal_decode_varlen.restype = c_int
+        lib.bifocal_prefill_unfused_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_i64]
+        lib.bifocal_prefill_unfused_workspace_bytes.restype = c_sz
+        lib.bifocal_prefill_unfused.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
+                                                c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
+        lib.bifocal_prefill_unfused.restype = c_int
+        lib.bifocal_decode_unfused_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_i64]
+        lib.bifocal_decode_unfused_workspace_bytes.restype = c_sz
+        lib.bifocal_decode_unfused.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
+                                               c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
+        lib.bifocal_decode_unfused.restype = c_int
         lib.bifocal_positions.argtypes = [c_i64, c_i64, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32), c_vp]
         lib.bifocal_positions.restype = c_int
@@ -189,6 +203,38 @@ def bifocal_decode_varlen(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_he
                                    _stream(stream))
     if st != 0:
         raise BifocalError(st, "bifocal_decode_varlen")
+
+
+def bifocal_prefill_unfused_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                                            L: int) -> int:
+    return int(load_library().bifocal_prefill_unfused_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+                                                                      int(L)))
+
+
+def bifocal_prefill_unfused(q, k, v, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, w0, w_pretrained,
+                            rope_theta, workspace, workspace_bytes, stream=None) -> None:
+    lib = load_library()
+    st = lib.bifocal_prefill_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), batch, n_q_heads, n_kv_heads,
+                                     head_dim, int(L), int(w0), int(w_pretrained), float(rope_theta), _ptr(workspace),
+                                     int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise BifocalError(st, "bifocal_prefill_unfused")
+
+
+def bifocal_decode_unfused_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                                           cache_capacity: int) -> int:
+    return int(load_library().bifocal_decode_unfused_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+                                                                     int(cache_capacity)))
+
+
+def bifocal_decode_unfused(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, cache_capacity,
+                           w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream=None) -> None:
+    lib = load_library()
+    st = lib.bifocal_decode_unfused(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _fptr(lse), batch, n_q_heads,
+                                    n_kv_heads, head_dim, int(L), int(cache_capacity), int(w0), int(w_pretrained),
+                                    float(rope_theta), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise BifocalError(st, "bifocal_decode_unfused")
 
 
 def bifocal_positions(L, w_pretrained, f_out, G_out, stream=None) -> None:
@@ -350,6 +396,53 @@ def decode_varlen(q, k_cache, v_cache, seq_lens, *, max_len: int, w0: int, w_pre
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     bifocal_decode_varlen(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, seq_lens, max_len, cap, w0, w_pretrained,
                           rope_theta, workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def prefill_unfused(q, k, v, *, w0: int, w_pretrained: int, rope_theta: float, out=None, lse=None,
+                    want_lse: bool = False, workspace=None, stream=None):
+    """The three-pass form of `prefill` (same shapes and result); allocates its workspace when
+    none is given."""
+    import torch
+
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, 4)
+    B, L, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != L or k.shape[3] != D:
+        raise ValueError("k/v shapes do not match q")
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(bifocal_prefill_unfused_workspace_bytes(B, Hq, k.shape[2], D, L), 4),
+                                dtype=torch.uint8, device=q.device)
+    bifocal_prefill_unfused(q, k, v, out, lse, B, Hq, k.shape[2], D, L, w0, w_pretrained, rope_theta, workspace,
+                            workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def decode_unfused(q, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, rope_theta: float, workspace=None,
+                   out=None, lse=None, want_lse: bool = False, stream=None):
+    """The three-pass form of `decode` (same shapes and result)."""
+    import torch
+
+    _check(q, "q", 3)
+    _check(k_cache, "k_cache", 4)
+    _check(v_cache, "v_cache", 4)
+    B, Hq, D = q.shape
+    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shapes do not match q")
+    if workspace is None:
+        workspace = torch.empty(max(bifocal_decode_unfused_workspace_bytes(B, Hq, Hkv, D, cap), 4),
+                                dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    bifocal_decode_unfused(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained, rope_theta,
+                           workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     return (out, lse) if (want_lse or lse is not None) else out
 
 

@@ -39,6 +39,38 @@ int map_hip(hipError_t e) { return e == hipSuccess ? BIFOCAL_OK : BIFOCAL_EHIP; 
 
 bool sane_theta(double t) { return t > 0.0 && isfinite(t); }
 
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Workspace of the unfused three-pass forms: the remote query and key copies, the three pass
+// outputs and their LSEs, and (decode) the split workspace the passes share.
+struct UnfusedLayout {
+  size_t qrem, krem, o[3], l[3], dws, total;
+};
+
+UnfusedLayout unfused_layout(size_t q_rows, size_t k_rows, int n_q_heads, int n_kv_heads, int head_dim,
+                             size_t lse_count, size_t dws_bytes) {
+  UnfusedLayout u;
+  const size_t qb = align256(q_rows * n_q_heads * head_dim * 2);
+  const size_t kb = align256(k_rows * n_kv_heads * head_dim * 2);
+  const size_t lb = align256(lse_count * 4);
+  size_t at = 0;
+  u.qrem = at;
+  at += qb;
+  u.krem = at;
+  at += kb;
+  for (int x = 0; x < 3; ++x) {
+    u.o[x] = at;
+    at += qb;
+  }
+  for (int x = 0; x < 3; ++x) {
+    u.l[x] = at;
+    at += lb;
+  }
+  u.dws = at;
+  u.total = at + align256(dws_bytes);
+  return u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,6 +245,110 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
                      cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream);
 }
 
+size_t bifocal_prefill_unfused_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int64_t L) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || !supported_head_dim(head_dim) || L < 1 || L > kMaxL)
+    return 0;
+  const long double elems = (long double)batch * (long double)L * n_q_heads * head_dim;
+  if (elems >= 1.0e17L) return 0;
+  const size_t rows = static_cast<size_t>(batch) * static_cast<size_t>(L);
+  return unfused_layout(rows, rows, n_q_heads, n_kv_heads, head_dim, rows * n_q_heads, 0).total;
+}
+
+int bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                            int n_q_heads, int n_kv_heads, int head_dim, int64_t L, int64_t w0, int64_t w_pretrained,
+                            double rope_theta, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o) return BIFOCAL_EINVAL;
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
+  if (L < 1 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
+  if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
+  if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
+  if (L > kMaxL) return BIFOCAL_EUNSUPPORTED;
+  const size_t need = bifocal_prefill_unfused_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L);
+  if (need == 0) return BIFOCAL_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < need) return BIFOCAL_EWORKSPACE;
+
+  const size_t rows = static_cast<size_t>(batch) * static_cast<size_t>(L);
+  const UnfusedLayout u = unfused_layout(rows, rows, n_q_heads, n_kv_heads, head_dim, rows * n_q_heads, 0);
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t G = bifocal_group_size(L, w_pretrained);
+  const int w = static_cast<int>(w0 < L ? w0 : L);
+  uint32_t W[64];
+  phase_increments(head_dim, rope_theta, W);
+
+  // Remote vectors q' = R(Delta_i) q~ and k' = R(Delta_j) k~, materialised.
+  bifocal::RotateRowsLaunch r;
+  r.batch = batch;
+  r.rows = static_cast<int>(L);
+  r.head_dim = head_dim;
+  r.src_cap = r.dst_cap = static_cast<int>(L);
+  r.pos0 = 0;
+  r.G = static_cast<int>(G);
+  r.W = W;
+  r.src = q;
+  r.dst = ws + u.qrem;
+  r.heads = n_q_heads;
+  int e = map_hip(bifocal::launch_rotate_rows(r, st));
+  if (e != BIFOCAL_OK) return e;
+  r.src = k;
+  r.dst = ws + u.krem;
+  r.heads = n_kv_heads;
+  e = map_hip(bifocal::launch_rotate_rows(r, st));
+  if (e != BIFOCAL_OK) return e;
+
+  // Three plain attention passes: A (window, base), B (causal, remote), C (window, remote).
+  bifocal::PrefillLaunch p;
+  p.krot = nullptr;
+  p.v = v;
+  p.batch = batch;
+  p.n_q_heads = n_q_heads;
+  p.n_kv_heads = n_kv_heads;
+  p.head_dim = head_dim;
+  p.L = p.Lq = p.kv_cap = static_cast<int>(L);
+  p.G = 1;
+  p.scale_log2 = scale_log2_for(head_dim);
+  p.W = W;
+  p.local_only = true;
+  const void* pq[3] = {q, ws + u.qrem, ws + u.qrem};
+  const void* pk[3] = {k, ws + u.krem, ws + u.krem};
+  const int pw[3] = {w, static_cast<int>(L), w};
+  for (int x = 0; x < 3; ++x) {
+    if (pw[x] == 0) continue;  // w0 = 0: passes A and C hold no pair
+    p.q = pq[x];
+    p.k = pk[x];
+    p.o = ws + u.o[x];
+    p.lse = reinterpret_cast<float*>(ws + u.l[x]);
+    p.w0 = pw[x];
+    e = map_hip(bifocal::launch_prefill(p, st));
+    if (e != BIFOCAL_OK) return e;
+  }
+
+  bifocal::Merge3Launch m;
+  m.oa = ws + u.o[0];
+  m.ob = ws + u.o[1];
+  m.oc = ws + u.o[2];
+  m.la = reinterpret_cast<const float*>(ws + u.l[0]);
+  m.lb = reinterpret_cast<const float*>(ws + u.l[1]);
+  m.lc = reinterpret_cast<const float*>(ws + u.l[2]);
+  m.o = o;
+  m.lse = lse;
+  m.batch = batch;
+  m.rows = static_cast<int>(L);
+  m.n_q_heads = n_q_heads;
+  m.head_dim = head_dim;
+  m.has_window = w > 0;
+  return map_hip(bifocal::launch_merge3(m, st));
+}
+
+size_t bifocal_decode_unfused_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                              int64_t cache_capacity) {
+  const size_t dws = bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, cache_capacity);
+  if (dws == 0 || cache_capacity > kMaxL) return 0;
+  const size_t b = static_cast<size_t>(batch);
+  return unfused_layout(b, b * static_cast<size_t>(cache_capacity), n_q_heads, n_kv_heads, head_dim,
+                        b * n_q_heads, dws).total;
+}
+
 int bifocal_decode_step(const void* q_raw, const void* k_raw, const void* v_new, void* k_cache, void* v_cache,
                         void* o, float* lse, int batch, int n_q_heads, int n_kv_heads, int head_dim,
                         int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained, double rope_theta,
@@ -246,6 +382,90 @@ int bifocal_decode_step(const void* q_raw, const void* k_raw, const void* v_new,
   // The rotated query sits in o; the reduce overwrites it only after the split kernel read it.
   return decode_impl(o, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, nullptr, L,
                      cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream, false);
+}
+
+int bifocal_decode_unfused(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int batch,
+                           int n_q_heads, int n_kv_heads, int head_dim, int64_t L, int64_t cache_capacity, int64_t w0,
+                           int64_t w_pretrained, double rope_theta, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  // Shapes and values are the decode's; the workspace is checked against this path's own size.
+  const int st0 = decode_impl(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, nullptr, L,
+                              cache_capacity, w0, w_pretrained, rope_theta, workspace, ~static_cast<size_t>(0),
+                              nullptr, /*check_only=*/true);
+  if (st0 != BIFOCAL_OK) return st0;
+  const size_t need = bifocal_decode_unfused_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, cache_capacity);
+  if (need == 0) return BIFOCAL_EUNSUPPORTED;
+  if (workspace_bytes < need) return BIFOCAL_EWORKSPACE;
+
+  const size_t b = static_cast<size_t>(batch);
+  const size_t dws_bytes = bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, cache_capacity);
+  const UnfusedLayout u = unfused_layout(b, b * static_cast<size_t>(cache_capacity), n_q_heads, n_kv_heads,
+                                         head_dim, b * n_q_heads, dws_bytes);
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t G = bifocal_group_size(L, w_pretrained);
+  const int64_t w = w0 < L ? w0 : L;
+  uint32_t W[64];
+  phase_increments(head_dim, rope_theta, W);
+
+  // The whole cache's remote keys k' = R(Delta_j) k~ (j < L) into a copy with the cache's
+  // layout, and the remote query q' = R(Delta_p) q~ at p = L - 1.
+  bifocal::RotateRowsLaunch r;
+  r.batch = batch;
+  r.head_dim = head_dim;
+  r.G = static_cast<int>(G);
+  r.W = W;
+  r.src = k_cache;
+  r.dst = ws + u.krem;
+  r.rows = static_cast<int>(L);
+  r.heads = n_kv_heads;
+  r.src_cap = r.dst_cap = static_cast<int>(cache_capacity);
+  r.pos0 = 0;
+  int e = map_hip(bifocal::launch_rotate_rows(r, st));
+  if (e != BIFOCAL_OK) return e;
+  r.src = q;
+  r.dst = ws + u.qrem;
+  r.rows = 1;
+  r.heads = n_q_heads;
+  r.src_cap = r.dst_cap = 1;
+  r.pos0 = static_cast<int>(L - 1);
+  e = map_hip(bifocal::launch_rotate_rows(r, st));
+  if (e != BIFOCAL_OK) return e;
+
+  // Three plain decode passes (G = 1, every pair local): A over the last w keys with base
+  // vectors, B over all L keys with remote vectors, C over the last w keys with remote vectors.
+  const size_t row_bytes = static_cast<size_t>(n_kv_heads) * head_dim * 2;
+  const size_t win_off = static_cast<size_t>(L - w) * row_bytes;
+  const char* kc = static_cast<const char*>(k_cache);
+  const char* vc = static_cast<const char*>(v_cache);
+  const char* kr = ws + u.krem;
+  const void* pq[3] = {q, ws + u.qrem, ws + u.qrem};
+  const void* pk[3] = {kc + win_off, kr, kr + win_off};
+  const void* pv[3] = {vc + win_off, vc, vc + win_off};
+  const int64_t pl[3] = {w, L, w};
+  for (int x = 0; x < 3; ++x) {
+    if (pl[x] == 0) continue;  // w0 = 0: passes A and C hold no pair
+    e = decode_impl(pq[x], pk[x], pv[x], ws + u.o[x], reinterpret_cast<float*>(ws + u.l[x]), batch, n_q_heads,
+                    n_kv_heads, head_dim, nullptr, pl[x], cache_capacity, pl[x], kMaxL, rope_theta, ws + u.dws,
+                    dws_bytes, stream);
+    if (e != BIFOCAL_OK) return e;
+  }
+
+  bifocal::Merge3Launch m;
+  m.oa = ws + u.o[0];
+  m.ob = ws + u.o[1];
+  m.oc = ws + u.o[2];
+  m.la = reinterpret_cast<const float*>(ws + u.l[0]);
+  m.lb = reinterpret_cast<const float*>(ws + u.l[1]);
+  m.lc = reinterpret_cast<const float*>(ws + u.l[2]);
+  m.o = o;
+  m.lse = lse;
+  m.batch = batch;
+  m.rows = 1;
+  m.n_q_heads = n_q_heads;
+  m.head_dim = head_dim;
+  m.has_window = w > 0;
+  return map_hip(bifocal::launch_merge3(m, st));
 }
 
 int bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

@@ -22,6 +22,7 @@ struct PrefillLaunch {
   int G;
   float scale_log2;      // log2(e) / sqrt(head_dim)
   const uint32_t* W;     // head_dim / 2 fixed-point phase increments (host memory)
+  bool local_only = false;  // one plain attention pass over the pairs 0 <= i - j < w0, no remote pass
 };
 
 struct DecodeLaunch {
@@ -55,7 +56,34 @@ struct RopeAppendLaunch {
   const uint32_t* W;
 };
 
+// Rows rotated by their correction offsets into a separate buffer: dst[b][r][h] =
+// R(Delta_{pos0 + r}) src[b][r][h] for r < rows (src_cap / dst_cap rows per batch).
+struct RotateRowsLaunch {
+  const void* src;
+  void* dst;
+  int batch, rows, heads, head_dim;
+  int src_cap, dst_cap, pos0, G;
+  const uint32_t* W;
+};
+
+// Inclusion-exclusion merge of three attention passes: O_X [batch, rows, n_q_heads, head_dim]
+// bf16, LSE_X [batch, n_q_heads, rows] fp32; has_window == false: passes A and C are empty.
+struct Merge3Launch {
+  const void* oa;
+  const void* ob;
+  const void* oc;
+  const float* la;
+  const float* lb;
+  const float* lc;
+  void* o;
+  float* lse;
+  int batch, rows, n_q_heads, head_dim;
+  bool has_window;
+};
+
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
+hipError_t launch_rotate_rows(const RotateRowsLaunch& p, hipStream_t stream);
+hipError_t launch_merge3(const Merge3Launch& p, hipStream_t stream);
 hipError_t launch_rope_append(const RopeAppendLaunch& r, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
 size_t prefill_workspace_bytes(long long batch, long long L, int n_kv_heads, int head_dim);

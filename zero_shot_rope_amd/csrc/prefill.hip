@@ -548,8 +548,9 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
   const long long nwg = (long long)p.batch * a.n_units * a.n_tiles;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   // With every pair local (w0 == L, which the host also sets for G == 1) there is no remote
-  // key: plain causal attention with no rotation at all.
-  if (p.w0 >= p.L) {
+  // key: plain causal attention with no rotation at all. local_only asks for that pass alone
+  // with w0 < L: plain sliding-window attention.
+  if (p.w0 >= p.L || p.local_only) {
     hipLaunchKernelGGL((prefill_kernel<D, kLocalOnly>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   } else if (p.krot != nullptr) {
     const long long rows = (long long)p.batch * p.L * p.n_kv_heads;
