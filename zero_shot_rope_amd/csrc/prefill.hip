@@ -172,13 +172,29 @@ void prefill_kernel(const PrefillArgs<D> a) {
   // (j > i) and their weights are 0.
   const int ld_row0 = RPI * T::NLDW * wave + lane / CPR;
   const int ld_slot = lane % CPR;
-  auto stage_direct = [&](const uint16_t* src, uint16_t* tile_lds, int j0) __attribute__((always_inline)) {
+  // Byte offset of each of this lane's direct loads within a tile: row * row stride + its
+  // swizzled chunk (loop-invariant, 32 bits). A tile entirely below L then needs no per-lane
+  // address arithmetic: its base (src + j0 rows) is wave-uniform and computed on the scalar unit.
+  uint32_t ld_off[T::NLDW];
 #pragma unroll
-    for (int n = 0; n < T::NLDW; ++n) {
-      const int row = ld_row0 + RPI * n;
-      const int j = min(j0 + row, L - 1);
-      load_lds16(src + (size_t)j * kv_row_stride + 8 * (ld_slot ^ swz<D>(row)),
-                 tile_lds + (RPI * T::NLDW * wave + RPI * n) * D);
+  for (int n = 0; n < T::NLDW; ++n) {
+    const int row = ld_row0 + RPI * n;
+    ld_off[n] = (uint32_t)(row * (int)kv_row_stride + 8 * (ld_slot ^ swz<D>(row))) * 2u;
+  }
+  auto stage_direct = [&](const uint16_t* src, uint16_t* tile_lds, int j0) __attribute__((always_inline)) {
+    if (j0 + kBN <= L) {
+      const char* base = reinterpret_cast<const char*>(src + (size_t)j0 * kv_row_stride);
+#pragma unroll
+      for (int n = 0; n < T::NLDW; ++n)
+        load_lds16(base + ld_off[n], tile_lds + (RPI * T::NLDW * wave + RPI * n) * D);
+    } else {
+#pragma unroll
+      for (int n = 0; n < T::NLDW; ++n) {
+        const int row = ld_row0 + RPI * n;
+        const int j = min(j0 + row, L - 1);
+        load_lds16(src + (size_t)j * kv_row_stride + 8 * (ld_slot ^ swz<D>(row)),
+                   tile_lds + (RPI * T::NLDW * wave + RPI * n) * D);
+      }
     }
   };
   // Fused mode: thread -> (key, 8-pair chunk) unit, rotated in registers, written swizzled.
@@ -214,6 +230,15 @@ void prefill_kernel(const PrefillArgs<D> a) {
   // and keys 16ch + 4h + 0..3 (+8 for elements 4..7); lane r of the group names 4 values of
   // row 16ch + 4h + r/4 (+8) at d = 32db + 16(g%2) + 4(r%4).
   const int k_sw = swz<D>(col);
+  // Element offset of this lane's K operand chunk c within a half tile: row col, chunk 2c + h
+  // swizzled. Kept in registers and hidden from the optimiser, so each operand read is one
+  // register plus an immediate (the buffer and the half tile), with no address add per read.
+  int k_off[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    k_off[c] = col * D + 8 * ((2 * c + h) ^ k_sw);
+    asm volatile("" : "+v"(k_off[c]));
+  }
   const int tr_r = lane & 15;
   const int tr_key = 4 * h + (tr_r >> 2);
   const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (tr_r & 3);
@@ -224,10 +249,10 @@ void prefill_kernel(const PrefillArgs<D> a) {
   // (8 MFMAs).
   auto qk = [&](const uint16_t* ks, int kb, const u32x4 (&qa)[NC], f32x16& s) __attribute__((always_inline)) {
     s = f32x16{};
-    const uint16_t* krow = ks + (32 * kb + col) * D;
+    const uint16_t* khalf = ks + 32 * kb * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const u32x4 av = *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * c + h) ^ k_sw));
+      const u32x4 av = *reinterpret_cast<const u32x4*>(khalf + k_off[c]);
       s = mfma32(av, qa[c], s);
     }
   };
@@ -306,9 +331,9 @@ void prefill_kernel(const PrefillArgs<D> a) {
                        u32x4 (&pb_cur)[2], bool local_pass) __attribute__((always_inline)) {
     constexpr bool DO_QK = decltype(do_qk)::value, DO_PV = decltype(do_pv)::value;
     constexpr int NS = NC + 2 * NDB;  // slots: NC score MFMAs, then 2 * NDB PV MFMAs
-    const uint16_t* krow = ks + (32 * kb_k + col) * D;
+    const uint16_t* khalf = ks + 32 * kb_k * D;
     auto read_k = [&](int c) __attribute__((always_inline)) {
-      return *reinterpret_cast<const u32x4*>(krow + 8 * ((2 * c + h) ^ k_sw));
+      return *reinterpret_cast<const u32x4*>(khalf + k_off[c]);
     };
     auto read_v = [&](int i) __attribute__((always_inline)) {
       const int ch = i / NDB, db = i % NDB;
