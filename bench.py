@@ -55,7 +55,7 @@ def parse():
 # otherwise the kernel changed since the counters were taken and the traffic is reported as null.
 MEASURED_TRAFFIC = {
     # rotate_keys_kernel + prefill_kernel<128, prerotated> at the 128K Qwen3-8B shape.
-    "prefill": {"sources": "fc1c335ba83589fe", "fetch_bytes": 20730.07e6, "write_bytes": 2105.47e6},
+    "prefill": {"sources": "0fb14a9076c7c207", "fetch_bytes": 20316.50e6, "write_bytes": 1774.79e6},
     # decode_split_kernel + decode_reduce_kernel, mean over the 512 steps (L 98001..98512).
     "decode": {"sources": "c76a924f99075640", "fetch_bytes": 407.09e6, "write_bytes": 4.34e6},
 }
