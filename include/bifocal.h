@@ -163,8 +163,11 @@ size_t bifocal_decode_varlen_workspace_bytes(int batch, int n_q_heads, int n_kv_
  *             1 <= max_len <= cache_capacity
  *   q, k_cache, v_cache, o, lse, w0, w_pretrained, rope_theta, stream: as bifocal_decode;
  *   workspace >= bifocal_decode_varlen_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
- *             max_len) (each sequence is split into key chunks as if it were decoded alone).
- * Sequence b's output equals bifocal_decode of that sequence alone at L = L_b.
+ *             max_len).
+ * The device cuts the whole batch's keys into chunks of one length, chosen from the lengths so
+ * that every chunk fits one grid of about one workgroup per CU, whatever the mix of lengths.
+ * Sequence b's output is bifocal_decode of that sequence alone at L = L_b, up to the rounding
+ * of a different chunking (the partials merge in another order).
  * Returns BIFOCAL_OK or a negative bifocal_status (BIFOCAL_EINVAL when seq_lens is NULL). */
 int bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                           int batch, int n_q_heads, int n_kv_heads, int head_dim,

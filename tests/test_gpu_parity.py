@@ -478,6 +478,9 @@ SMALL_VARLEN = [
     (700, 8, 2, 64, 64, 17, 1e4, [700, 33, 64]),
     (3000, 32, 8, 128, 1000, 128, 1e6, [2000, 3000, 1001, 129]),               # Qwen3-8B heads
     (500, 4, 4, 128, 100, 0, 1e4, [450, 101, 7]),                                # all remote
+    # 70 sequences (more than one 64-wide scan step), lengths 1..300 spread by a fixed rule
+    (300, 4, 1, 64, 64, 10, 1e4, [1 + (37 * i * i + 11 * i) % 300 for i in range(70)]),
+    (4000, 8, 2, 128, 512, 64, 1e6, [4000] + [1] * 5 + [33] * 5),               # one long, many tiny
 ]
 
 
@@ -511,7 +514,7 @@ def test_decode_varlen_small(case):
         assert np.max(np.abs(lse[b:b + 1] - ref_lse)) <= LSE_ABS
 
 
-def test_decode_varlen_equal_lengths_is_decode():
+def test_decode_varlen_equal_lengths_matches_decode():
     B, cap, Hq, Hkv, D, wp, w0, theta, L = 3, 900, 8, 2, 128, 200, 60, 1e6, 777
     rng = np.random.default_rng(12)
     kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
@@ -519,7 +522,10 @@ def test_decode_varlen_equal_lengths_is_decode():
     qb = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
     o_u, lse_u = run_decode(qb, kb, vb, L, w0, wp, theta)
     o_v, lse_v = run_decode_varlen(qb, kb, vb, [L] * B, L, w0, wp, theta)
-    assert np.array_equal(o_u, o_v) and np.array_equal(lse_u, lse_v)
+    # Same attention, chunked differently: equal up to the order the partials merge in.
+    assert np.max(np.abs(o_u - o_v)) <= 4e-3 and np.max(np.abs(lse_u - lse_v)) <= 1e-4
+    ref_o, _ = bifocal_decode(f64(qb), f64(kb), f64(vb), L=L, w0=w0, w_pretrained=wp, theta=theta)
+    compare(o_v, ref_o, "varlen o")
 
 
 def test_decode_varlen_clamps_lengths():

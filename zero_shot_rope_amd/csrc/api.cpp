@@ -180,8 +180,10 @@ size_t bifocal_decode_varlen_workspace_bytes(int batch, int n_q_heads, int n_kv_
                                              int64_t max_len) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1 || max_len < 1) return 0;
   if (max_len > kMaxL || n_q_heads % n_kv_heads != 0) return 0;
-  const bifocal::DecodeSplit s = bifocal::decode_split(max_len, 1, n_kv_heads);
-  return static_cast<size_t>(batch) * n_q_heads * s.max_splits * (head_dim + 2) * sizeof(float);
+  // One slot per workgroup of the batch-wide chunking, for every sequence (a sequence can own at
+  // most all of them); independent of the lengths, which only the device knows.
+  const long long slots = bifocal::decode_varlen_slots(batch, n_kv_heads);
+  return static_cast<size_t>(batch) * n_q_heads * slots * (head_dim + 2) * sizeof(float);
 }
 
 // Shared by the single-length and the per-sequence-length decode. lens == NULL: every sequence has
@@ -199,8 +201,9 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   const int group = n_q_heads / n_kv_heads;
   if (group != 1 && group != 2 && group != 4) return BIFOCAL_EUNSUPPORTED;
   if (cache_capacity > kMaxL || batch > 65535) return BIFOCAL_EUNSUPPORTED;  // grid z limit
-  if (lens != nullptr && (long long)batch * bifocal::decode_split(L, 1, n_kv_heads).max_splits > 0x7fffffffLL)
-    return BIFOCAL_EUNSUPPORTED;  // grid x limit of the interleaved per-sequence grid
+  if (lens != nullptr && (long double)batch * n_q_heads * bifocal::decode_varlen_slots(batch, n_kv_heads) *
+                               (head_dim + 2) * 4 >= 4.0e18L)
+    return BIFOCAL_EUNSUPPORTED;  // workspace size beyond size_t arithmetic
   const size_t need = lens ? bifocal_decode_varlen_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L)
                            : bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L);
   if (!workspace || workspace_bytes < need) return BIFOCAL_EWORKSPACE;
@@ -210,8 +213,9 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   uint32_t W[64];
   phase_increments(head_dim, rope_theta, W);
   // One length: the batch shares one grid of about one workgroup per CU. Per-sequence lengths:
-  // each sequence is split as if it were alone (its chunks exist up to its own length).
-  const bifocal::DecodeSplit s = bifocal::decode_split(L, lens ? 1 : batch, n_kv_heads);
+  // the device cuts the whole batch's keys into chunks of one length, over a grid of
+  // decode_varlen_slots workgroups.
+  const bifocal::DecodeSplit s = bifocal::decode_split(L, batch, n_kv_heads);
   bifocal::DecodeLaunch p;
   p.q = q;
   p.k_cache = k_cache;
@@ -230,8 +234,8 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   else p.w0 = static_cast<int>(w0 < L ? w0 : L);  // clamped per sequence on the device
   p.G = static_cast<int>(G);
   p.w_pretrained = static_cast<int>(w_pretrained < (1LL << 30) ? w_pretrained : (1LL << 30));
-  p.n_splits = s.n_splits;
-  p.chunk = s.chunk;
+  p.n_splits = lens ? static_cast<int>(bifocal::decode_varlen_slots(batch, n_kv_heads)) : s.n_splits;
+  p.chunk = s.chunk;  // unused with per-sequence lengths
   p.scale_log2 = scale_log2_for(head_dim);
   p.W = W;
   return map_hip(bifocal::launch_decode(p, static_cast<hipStream_t>(stream)));

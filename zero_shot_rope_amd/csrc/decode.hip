@@ -10,6 +10,8 @@
 //   double-buffered swizzled tile read back transposed for O^T = V^T P^T. Local and remote
 //   contributions share one running max; the wave writes the partial (max, sum, unnormalised
 //   output) of its chunk to the workspace.
+// Per-sequence lengths: one chunk length for the whole batch, chosen on the device from the
+//   lengths so that every chunk of every sequence fits one grid of about one workgroup per CU.
 // Reduce kernel: merges the partials of all chunks by log-sum-exp and writes bf16 o / lse.
 #include <type_traits>
 
@@ -63,6 +65,52 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Per-sequence lengths: the batch's keys are cut into chunks of one length, chosen from the
+// device-side lengths so that sum_b ceil(L_b / chunk) <= slots (the grid's x size, target + B):
+// chunk = max(32, total / (slots - B) rounded up to a multiple of 32), since
+// sum_b ceil(L_b / chunk) <= total / chunk + B. Every workgroup then carries about the same
+// number of keys, whatever the mix of lengths. Lengths are clamped to [1, maxL].
+__device__ __forceinline__ int varlen_len(const int32_t* lens, int i, int maxL) { return min(max(lens[i], 1), maxL); }
+
+// Run by one wave: the chunk length (and, with want >= 0, the sequence and split of workgroup
+// `want`; b_out = -1 when it has no chunk). Lanes take 64 sequences at a time.
+__device__ __forceinline__ int varlen_plan(const int32_t* lens, int B, int maxL, int slots, int want, int& b_out,
+                                           int& split_out) {
+  const int lane = threadIdx.x & 63;
+  long long tot = 0;
+  for (int i0 = 0; i0 < B; i0 += 64) tot += (i0 + lane < B) ? varlen_len(lens, i0 + lane, maxL) : 0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+  const long long per = (tot + (slots - B) - 1) / (slots - B);
+  // Never longer than the longest sequence needs (one chunk each then, B <= slots).
+  const long long cap = ((long long)maxL + 31) / 32 * 32;
+  const int chunk = (int)min(cap, max(32LL, (per + 31) / 32 * 32));
+  b_out = -1;
+  split_out = 0;
+  if (want < 0) return chunk;
+  int base = 0;  // first split index of the current 64 sequences
+  for (int i0 = 0; i0 < B && b_out < 0; i0 += 64) {
+    const int i = i0 + lane;
+    const int n = (i < B) ? (varlen_len(lens, i, maxL) + chunk - 1) / chunk : 0;
+    int incl = n;  // inclusive prefix over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int up = __shfl_up(incl, off);
+      if (lane >= off) incl += up;
+    }
+    const int excl = base + incl - n;
+    const bool mine = (i < B) && want >= excl && want < excl + n;
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(mine);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      b_out = i0 + src;
+      split_out = want - __shfl(excl, src);
+    }
+    base += __shfl(incl, 63);
+  }
+  return chunk;
+}
+
 template <int D>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(const DecodeArgs<D> a) {
@@ -81,11 +129,29 @@ void decode_split_kernel(const DecodeArgs<D> a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;  // MFMA 16x16 lane = li + 16 * lg
-  // One length: grid (split, KV-head group, batch). Per-sequence lengths: the sequences are
-  // interleaved along x (b = x % batch, split = x / batch) so long and short sequences' chunks mix
-  // in the dispatch order.
-  const int split = a.lens ? (int)blockIdx.x / a.B : (int)blockIdx.x;
-  const int b = a.lens ? (int)blockIdx.x % a.B : (int)blockIdx.z;
+  // One length: grid (split, KV-head group, batch). Per-sequence lengths: grid (slot, KV-head
+  // group); wave 0 maps the slot to a (sequence, split) of the batch-wide chunking, and slots past
+  // the last chunk exit.
+  int split = (int)blockIdx.x, b = (int)blockIdx.z, chunk = a.chunk;
+  if (a.lens != nullptr) {
+    // The plan travels through the second angle table, which is first written after the first
+    // block's barrier, long after every wave has read it here.
+    int* s_plan = reinterpret_cast<int*>(s_t1);
+    if (wave == 0) {
+      int pb, ps;
+      const int c = varlen_plan(a.lens, a.B, a.L, a.n_splits, (int)blockIdx.x, pb, ps);
+      if (lane == 0) {
+        s_plan[0] = pb;
+        s_plan[1] = ps;
+        s_plan[2] = c;
+      }
+    }
+    __syncthreads();
+    b = s_plan[0];
+    split = s_plan[1];
+    chunk = s_plan[2];
+    if (b < 0) return;
+  }
   const int g = blockIdx.y * kDecWaves + wave;  // KV head of this wave
   const bool head_live = g < a.Hkv;
   const int gl = head_live ? g : 0;
@@ -100,20 +166,6 @@ void decode_split_kernel(const DecodeArgs<D> a) {
     if (G == 1 || w0 >= L) w0 = L;
   }
   const int p = L - 1;
-  // A chunk past this sequence's end holds no key: its partial is empty (max -inf, sum 0, O 0).
-  if (split * a.chunk >= L) {
-    if (head_live && li < Hg) {
-      float* dst = a.ws + (((size_t)b * a.Hq + (size_t)g * Hg + li) * a.n_splits + split) * (D + 2);
-      if (lg == 0) {
-        dst[0] = kNegBig;
-        dst[1] = 0.f;
-      }
-      for (int d = 4 * lg; d < D; d += 16)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[2 + d + r] = 0.f;
-    }
-    return;
-  }
 
   // Query operands (B of S^T = K Q^T): column li = query head g*Hg + li (zero if li >= Hg), rows
   // d = 32c + 8lg .. +8, scaled into log2 units: qs = q~ for local keys, qr = R(Delta_p) q~ for
@@ -142,8 +194,8 @@ void decode_split_kernel(const DecodeArgs<D> a) {
   const size_t row_stride = (size_t)a.Hkv * D;
   const uint16_t* kbase = a.kc + (size_t)b * a.cap * row_stride + (size_t)gl * D;
   const uint16_t* vbase = a.vc + (size_t)b * a.cap * row_stride + (size_t)gl * D;
-  const int k_begin = split * a.chunk;
-  const int k_end = min(L, k_begin + a.chunk);
+  const int k_begin = split * chunk;
+  const int k_end = min(L, k_begin + chunk);
   const int nblk = (k_end - k_begin + kDecBlock - 1) / kDecBlock;
   // LDS buffers are named statically (buffer 0/1 of V and of the angle table) and indexed with
   // one integer offset, so the compiler can tell every LDS read from the direct loads in flight
@@ -386,17 +438,30 @@ constexpr int kRedGroups = kRedThreads / 32;
 
 template <int D>
 __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
-                                                                    float* __restrict__ lse, int Hq, int n_splits) {
+                                                                    float* __restrict__ lse, int Hq, int n_splits,
+                                                                    const int32_t* __restrict__ lens, int B, int maxL) {
   __shared__ float s_m[kRedThreads / 64];
   __shared__ float s_row[kRedThreads][33];  // per thread: 32 rescaled outputs, then the rescaled sum
   __shared__ float s_grp[kRedGroups][33];
   const int head = blockIdx.x, slice = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
+  // n_splits is the slot stride; with per-sequence lengths this sequence has ceil(L_b / chunk).
+  int n_have = n_splits;
+  if (lens != nullptr) {
+    __shared__ int s_n;
+    if (wave == 0) {
+      int pb, ps;
+      const int chunk = varlen_plan(lens, B, maxL, n_splits, -1, pb, ps);
+      if (lane == 0) s_n = (varlen_len(lens, b, maxL) + chunk - 1) / chunk;
+    }
+    __syncthreads();
+    n_have = s_n;
+  }
   const float* src = ws + ((size_t)b * Hq + head) * n_splits * (D + 2);
   float m = kNegBig, l = 0.f, acc[32];
 #pragma unroll
   for (int d = 0; d < 32; ++d) acc[d] = 0.f;
-  for (int sp = t; sp < n_splits; sp += kRedThreads) {
+  for (int sp = t; sp < n_have; sp += kRedThreads) {
     const float* ps = src + (size_t)sp * (D + 2);
     const float ms = ps[0], ls = ps[1];
     f32x4 v[8];
@@ -451,6 +516,11 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
   }
 }
 
+long long decode_varlen_slots(int batch, int n_kv_heads) {
+  const long long groups = (n_kv_heads + kDecWaves - 1) / kDecWaves;
+  return (256 + groups - 1) / groups + batch;
+}
+
 DecodeSplit decode_split(long long L, int batch, int n_kv_heads) {
   // One 8-wave workgroup per CU (its V tiles use 128 KB of LDS): aim for 256 workgroups.
   const long long groups = (long long)batch * ((n_kv_heads + kDecWaves - 1) / kDecWaves);
@@ -486,12 +556,15 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
   for (int i = 0; i < D / 2; ++i) a.W[i] = p.W[i];
   a.B = p.batch;
   const unsigned groups = (p.n_kv_heads + kDecWaves - 1) / kDecWaves;
-  const dim3 grid = p.lens ? dim3(p.n_splits * p.batch, groups, 1) : dim3(p.n_splits, groups, p.batch);
+  // Per-sequence lengths: n_splits is the number of slots (workgroups along x) of the batch-wide
+  // chunking, and the slot stride of the workspace.
+  const dim3 grid = p.lens ? dim3(p.n_splits, groups, 1) : dim3(p.n_splits, groups, p.batch);
   hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(kDecThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, D / 32, p.batch), dim3(kRedThreads), 0, stream,
-                     (const float*)p.workspace, static_cast<uint16_t*>(p.o), p.lse, p.n_q_heads, p.n_splits);
+                     (const float*)p.workspace, static_cast<uint16_t*>(p.o), p.lse, p.n_q_heads, p.n_splits, p.lens,
+                     p.batch, p.L);
   return hipGetLastError();
 }
 

@@ -96,5 +96,7 @@ struct DecodeSplit {
   int max_splits;  // upper bound on n_splits for every length <= L (workspace sizing)
 };
 DecodeSplit decode_split(long long L, int batch, int n_kv_heads);
+// Workgroups along x (and workspace slots per sequence) of a per-sequence-length decode.
+long long decode_varlen_slots(int batch, int n_kv_heads);
 
 }  // namespace bifocal
