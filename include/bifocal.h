@@ -73,7 +73,9 @@ size_t bifocal_prefill_workspace_bytes(int batch, int n_kv_heads, int head_dim, 
  *           workspace must be ordered (same stream).
  * Row i attends keys 0..i; G is computed once from the full L for every row.
  * w0 >= L makes every pair local (plain causal RoPE attention); w0 = 0 makes every pair
- * remote. head_dim must be 64 or 128; n_q_heads must be a multiple of n_kv_heads.
+ * remote. head_dim must be 64 or 128; n_q_heads must be a multiple of n_kv_heads;
+ * n_kv_heads * head_dim below 2^24 (BIFOCAL_EUNSUPPORTED otherwise, also for the chunked and
+ * unfused prefill).
  * Limits: L <= 2^30, batch * L * heads * head_dim < 2^62.
  * Returns BIFOCAL_OK or a negative bifocal_status (BIFOCAL_EWORKSPACE when a non-NULL
  * workspace is smaller than required). */

@@ -82,6 +82,7 @@ def prefill_call(lib, **kw):
     (dict(theta=0.0), EINVAL), (dict(theta=-1.0), EINVAL), (dict(theta=float("nan")), EINVAL),
     (dict(theta=float("inf")), EINVAL), (dict(hq=6, hkv=4), EINVAL),
     (dict(d=96), EUNSUP), (dict(d=256), EUNSUP), (dict(L=(1 << 30) + 1), EUNSUP),
+    (dict(hq=1 << 17, hkv=1 << 17), EUNSUP),  # n_kv_heads * head_dim = 2^24: 32-bit tile offsets
     (dict(ws=FAKE, wsb=0), EWS), (dict(ws=FAKE, wsb=256 * 2 * 128 * 2 - 1), EWS),
 ])
 def test_prefill_rejects_before_any_hip_call(lib, kw, expect):

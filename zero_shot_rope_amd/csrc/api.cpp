@@ -39,6 +39,10 @@ int map_hip(hipError_t e) { return e == hipSuccess ? BIFOCAL_OK : BIFOCAL_EHIP; 
 
 bool sane_theta(double t) { return t > 0.0 && isfinite(t); }
 
+// The prefill kernels address a key/value tile row by a 32-bit byte offset (row < 64 times the
+// row stride n_kv_heads * head_dim elements).
+bool kv_row_fits(int n_kv_heads, int head_dim) { return (long long)n_kv_heads * head_dim < (1LL << 24); }
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace of the unfused three-pass forms: the remote query and key copies, the three pass
@@ -142,7 +146,7 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
   if (L < 1 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
   if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
   if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
-  if (L > kMaxL) return BIFOCAL_EUNSUPPORTED;
+  if (L > kMaxL || !kv_row_fits(n_kv_heads, head_dim)) return BIFOCAL_EUNSUPPORTED;
   const long double elems = (long double)batch * (long double)L * n_q_heads * head_dim;
   if (elems >= 4.0e18L) return BIFOCAL_EUNSUPPORTED;
   return prefill_impl(q, k, v, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, L, L, w0, w_pretrained,
@@ -160,7 +164,7 @@ int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cach
   if (cache_capacity < 1 || q_offset > cache_capacity - q_len) return BIFOCAL_EINVAL;  // L <= capacity
   if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
   if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
-  if (cache_capacity > kMaxL) return BIFOCAL_EUNSUPPORTED;
+  if (cache_capacity > kMaxL || !kv_row_fits(n_kv_heads, head_dim)) return BIFOCAL_EUNSUPPORTED;
   const long double elems = (long double)batch * (long double)cache_capacity * n_q_heads * head_dim;
   if (elems >= 4.0e18L) return BIFOCAL_EUNSUPPORTED;
   const int64_t L = q_offset + q_len;
@@ -266,7 +270,7 @@ int bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* o
   if (L < 1 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
   if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
   if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
-  if (L > kMaxL) return BIFOCAL_EUNSUPPORTED;
+  if (L > kMaxL || !kv_row_fits(n_kv_heads, head_dim)) return BIFOCAL_EUNSUPPORTED;
   const size_t need = bifocal_prefill_unfused_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L);
   if (need == 0) return BIFOCAL_EUNSUPPORTED;
   if (!workspace || workspace_bytes < need) return BIFOCAL_EWORKSPACE;
