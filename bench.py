@@ -396,6 +396,10 @@ def main():
                                "fused_over_unfused_throughput": round(unfused_ms / pre_avg, 3),
                                "unfused_over_control_throughput": round(ctrl_ms / unfused_ms, 3)},
         "decode": decode,
+        "context_from_pages": ("H100, other kernels and baselines, not comparable: fused prefill up to 1.39x "
+                               "FlashAttention-2 and 0.83-0.88x FlashAttention-3 at 64K-128K; single-batch decode "
+                               "within 4% of FlashAttention-2; unfused three-pass 0.29x; unfused decode 0.15-0.21x "
+                               "FlashAttention-3. Here: bifocal_over_control, fused_over_unfused_throughput."),
         "cpu_baseline": cpu,
     }
     if args.copy_calibration:
