@@ -166,10 +166,13 @@ void decode_split_kernel(const DecodeArgs<D> a) {
     if (G == 1 || w0 >= L) w0 = L;
   }
   const int p = L - 1;
+  const int dq = correction_offset(p, G);
 
-  // Query operands (B of S^T = K Q^T): column li = query head g*Hg + li (zero if li >= Hg), rows
-  // d = 32c + 8lg .. +8, scaled into log2 units: qs = q~ for local keys, qr = R(Delta_p) q~ for
-  // remote keys. Both stay in registers for the whole chunk.
+  // Query operand (B of S^T = K Q^T): column li = query head g*Hg + li (zero if li >= Hg), rows
+  // d = 32c + 8lg .. +8, the bf16 query as given, for local and remote keys alike. A remote score
+  // (R(Delta_p) q~) . (R(Delta_j) k~) equals q~ . R(Delta_j - Delta_p) k~ (the pair rotations
+  // compose additively), so only the key is rotated, once, and the query enters the products
+  // unrounded; the softmax scale is applied to the fp32 scores.
   const bool q_live = head_live && li < Hg;
   const uint16_t* qsrc = a.q + ((size_t)b * a.Hq + (size_t)gl * Hg + (q_live ? li : 0)) * D + 8 * lg;
   auto load_q = [&](u32x4 (&raw)[NQC]) __attribute__((always_inline)) {
@@ -181,15 +184,10 @@ void decode_split_kernel(const DecodeArgs<D> a) {
     for (int c = 0; c < NQC; ++c)
       if (!q_live) raw[c] = u32x4{0, 0, 0, 0};
   };
-  // The q loads are issued first; they are finished (scaled, rotated) after the first block's K
-  // and V loads are in flight, so the first cache block does not wait for them.
-  u32x4 qr[NQC], qs[NQC], qraw[NQC];
-  load_q(qraw);
-  uint32_t wq[NQC / 2][8];  // phase increments of this lane's query pairs
-#pragma unroll
-  for (int c = 0; c < NQC / 2; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) wq[c][e] = a.W[32 * c + 8 * lg + e];
+  // The q loads are issued first and masked after the first block's K and V loads are in
+  // flight, so the first cache block does not wait for them.
+  u32x4 qs[NQC];
+  load_q(qs);
 
   const size_t row_stride = (size_t)a.Hkv * D;
   const uint16_t* kbase = a.kc + (size_t)b * a.cap * row_stride + (size_t)gl * D;
@@ -232,7 +230,7 @@ void decode_split_kernel(const DecodeArgs<D> a) {
                  vtile(buf) + (vwave + RPI * n * D));
     }
   };
-  // Angle table of a block: row = key, (cos, sin) of Delta_j * omega_k at floats 2k, 2k+1, with
+  // Angle table of a block: row = key, (cos, sin) of (Delta_j - Delta_p) * omega_k at floats 2k, 2k+1, with
   // 16-byte chunk c of row r stored at chunk c ^ (r & 15) (16 rows read at one chunk hit 16
   // distinct bank groups). Thread t fills frequency t % HALF of keys t / HALF + (threads/HALF) n.
   const int t_k = tid % HALF, t_key0 = tid / HALF;
@@ -242,7 +240,7 @@ void decode_split_kernel(const DecodeArgs<D> a) {
     for (int n = 0; n < TPT; ++n) {
       const int key = t_key0 + (kDecThreads / HALF) * n;
       float sn, cs;
-      turns_sincos(phase_turns(correction_offset(min(blk + key, L - 1), G), t_w), sn, cs);
+      turns_sincos(phase_turns(correction_offset(min(blk + key, L - 1), G) - dq, t_w), sn, cs);
       *reinterpret_cast<f32x2*>(table(buf) + (key * D + 4 * ((t_k >> 1) ^ (key & 15)) + 2 * (t_k & 1))) =
           f32x2{cs, sn};
     }
@@ -276,7 +274,7 @@ void decode_split_kernel(const DecodeArgs<D> a) {
       }
     }
     if (has_rem) {
-      // Correction rotation R(Delta_j) of this lane's keys with the block's shared table, into
+      // Rotation R(Delta_j - Delta_p) of this lane's keys with the block's shared table, into
       // temporaries that feed the MFMAs directly (the loaded K registers stay read-only, so the
       // compiler never copies a register whose load may still be in flight).
       const float* tb = table(buf);
@@ -296,8 +294,8 @@ void decode_split_kernel(const DecodeArgs<D> a) {
             olo[w] = pack_bf16x2(x0 * tc[0] - y0 * tc[1], x1 * tc[2] - y1 * tc[3]);
             ohi[w] = pack_bf16x2(x0 * tc[1] + y0 * tc[0], x1 * tc[3] + y1 * tc[2]);
           }
-          t[kg] = mfma16(olo, qr[c], t[kg]);
-          t[kg] = mfma16(ohi, qr[c + NQC / 2], t[kg]);
+          t[kg] = mfma16(olo, qs[c], t[kg]);
+          t[kg] = mfma16(ohi, qs[c + NQC / 2], t[kg]);
         }
       }
 #pragma unroll
@@ -311,6 +309,9 @@ void decode_split_kernel(const DecodeArgs<D> a) {
         }
       }
     }
+    // Scores into log2 units (log2(e) / sqrt(D)), in fp32.
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) s[kg] *= a.scale_log2;
     if (blk + kDecBlock > k_end) {
 #pragma unroll
       for (int kg = 0; kg < 2; ++kg)
@@ -366,20 +367,8 @@ void decode_split_kernel(const DecodeArgs<D> a) {
   u32x4 ka[NKR], kb[NKR];
   load_v(k_begin, B0);
   load_k(k_begin, ka);
-  wait_vmcnt<NKR + NLD>();  // q and its phase increments are in; block 0 stays in flight
-  mask_q(qraw);
-#pragma unroll
-  for (int c = 0; c < NQC; ++c) qs[c] = scale8(qraw[c], a.scale_log2);
-  {
-    const int dq = correction_offset(p, G);
-#pragma unroll
-    for (int c = 0; c < NQC / 2; ++c) {
-      u32x4 lo = qraw[c], hi = qraw[c + NQC / 2];
-      rotate8_scaled(lo, hi, dq, wq[c], a.scale_log2);
-      qr[c] = lo;
-      qr[c + NQC / 2] = hi;
-    }
-  }
+  wait_vmcnt<NKR + NLD>();  // q is in; block 0 stays in flight
+  mask_q(qs);
   if (need_table) fill_table(k_begin, B0);
   lds_barrier();
   // MORE: a block i+1 exists (always true except for the chunk's last block).
