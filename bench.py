@@ -57,7 +57,7 @@ MEASURED_TRAFFIC = {
     # rotate_keys_kernel + prefill_kernel<128, prerotated> at the 128K Qwen3-8B shape.
     "prefill": {"sources": "0fb14a9076c7c207", "fetch_bytes": 20316.50e6, "write_bytes": 1774.79e6},
     # decode_split_kernel + decode_reduce_kernel, mean over the 512 steps (L 98001..98512).
-    "decode": {"sources": "e3cdc627749b731b", "fetch_bytes": 407.11e6, "write_bytes": 4.34e6},
+    "decode": {"sources": "7bdbc5f7d7f90da5", "fetch_bytes": 407.04e6, "write_bytes": 4.33e6},
 }
 # The files holding the measured kernels' device code and launch geometry.
 _KERNEL_SOURCES = {
