@@ -34,9 +34,11 @@
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query column, so the row max
 //   and sum are in-lane plus one v_permlane32_swap; P^T feeds the PV MFMA from registers;
 //   the V^T operand comes from ds_read_b64_tr_b16 on the row-major V tile; O^T accumulates
-//   in 64 registers per lane. Q is pre-scaled by log2(e)/sqrt(D), so scores arrive in log2
-//   units. The running max is only raised when a tile's max exceeds it by more than kSlack
-//   (the output is rescaled then); otherwise exponents stay <= kSlack.
+//   in 64 registers per lane. Q enters the products as given (unscaled) and the softmax scale
+//   log2(e)/sqrt(D) is folded into the exponent, exp2(fma(s, scale, -m)), so the local scores
+//   carry no rounding of a scaled query. The running max (log2 units) is only raised when a
+//   tile's max exceeds it by more than kSlack (the output is rescaled then); otherwise
+//   exponents stay <= kSlack.
 //   Workgroup ids are remapped so that each of the 8 XCDs owns a contiguous range of
 //   (batch, head unit, query tile) work, longest causal rows first.
 #include <type_traits>
@@ -74,6 +76,12 @@ constexpr int kThreads = 64 * kWaves;
 // row sums <= 2^81 over 2^17 keys, far inside fp32 and bf16 range, so after a row's first tile
 // the max (and the rescale of O) practically never moves.
 constexpr float kSlack = 64.0f;
+// Scores are kept unscaled (the query enters the products as given) and the softmax scale
+// log2(e)/sqrt(D) is folded into the exponent, exp2(fma(s, scale, -m)). The running max m is in
+// log2 units. A half tile's raw max starts from kMaskedMax, far above the masked value kNegBig
+// and far below any real score, so a fully masked half tile can only set m to kMaskedMax * scale,
+// against which a masked score still has exponent below -1e28 (weight exactly 0).
+constexpr float kMaskedMax = -1.0e20f;
 
 template <int D>
 struct Tile {
@@ -132,8 +140,8 @@ void prefill_kernel(const PrefillArgs<D> a) {
 
   const size_t q_row_stride = (size_t)a.Hq * D;
   const int qi = iw + col;  // this lane's query row
-  // Query operand (B of S^T = K Q^T): lane (col, h) holds q[qi][16c + 8h .. +8], scaled into
-  // log2 units; with `rotate` the correction rotation R(Delta_qi) is applied first.
+  // Query operand (B of S^T = K Q^T): lane (col, h) holds q[qi][16c + 8h .. +8] as given; with
+  // `rotate`, the correction rotation R(Delta_qi) of it (in fp32, rounded once to bf16).
   auto load_q = [&](bool rotate, u32x4 (&dst)[NC]) __attribute__((always_inline)) {
     const uint16_t* src = a.q + ((size_t)b * a.Lq + (qi - a.q0)) * q_row_stride + (size_t)head * D + 8 * h;
     u32x4 raw[NC];
@@ -147,13 +155,13 @@ void prefill_kernel(const PrefillArgs<D> a) {
 #pragma unroll
       for (int c = 0; c < NC / 2; ++c) {
         u32x4 lo = raw[c], hi = raw[c + NC / 2];
-        rotate8_scaled(lo, hi, dq, &s_w[16 * c + 8 * h], qscale);
+        rotate8(lo, hi, dq, &s_w[16 * c + 8 * h]);
         dst[c] = lo;
         dst[c + NC / 2] = hi;
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) dst[c] = scale8(raw[c], qscale);
+      for (int c = 0; c < NC; ++c) dst[c] = raw[c];
     }
   };
 
@@ -276,31 +284,12 @@ void prefill_kernel(const PrefillArgs<D> a) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int r = 8 * ch + 2 * w;
-        const uint32_t pk = pack_bf16x2(fast_exp2(s[r] - m_run), fast_exp2(s[r + 1] - m_run));
+        const uint32_t pk = pack_bf16x2(fast_exp2(__builtin_fmaf(s[r], qscale, -m_run)),
+                                        fast_exp2(__builtin_fmaf(s[r + 1], qscale, -m_run)));
         pb[ch][w] = pk;
         ps = sum_bf16x2(pk, ps);
       }
     return ps;
-  };
-  // Online softmax of one half tile: exponentials against the stored max; when some score
-  // exceeds it by more than kSlack (always on a row's first tile), raise the max to the column's,
-  // rescale O and the sums, and redo the exponentials. Adds the row sum to the pass's weight.
-  auto softmax = [&](const f32x16& s, u32x4 (&pb)[2], bool local_pass) __attribute__((always_inline)) {
-    float mxl = kNegBig;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mxl = max3f(mxl, s[r], s[r + 1]);
-    float ps = exps(s, pb);
-    if (wave_any(mxl > m_run + kSlack)) {
-      const float m_new = __builtin_fmaxf(m_run, pair_max(mxl));
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_pass[0] *= alpha;
-      l_pass[1] *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      ps = exps(s, pb);
-    }
-    l_pass[local_pass ? 0 : 1] += ps;
   };
   auto pv = [&](const uint16_t* vs, int kb, const u32x4 (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -353,7 +342,7 @@ void prefill_kernel(const PrefillArgs<D> a) {
     u32x4 op[NS];
 #pragma unroll
     for (int m = 0; m < AHEAD; ++m) op[m] = read_op(m);
-    float mxl = kNegBig, ps = 0.f, e0 = 0.f, e1 = 0.f;
+    float mxl = kMaskedMax, ps = 0.f, e0 = 0.f, e1 = 0.f;
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
       __builtin_amdgcn_sched_barrier(0);
@@ -370,8 +359,8 @@ void prefill_kernel(const PrefillArgs<D> a) {
       for (int k = (16 * m) / NS; k < (16 * (m + 1)) / NS; ++k) {
         const int pr = k >> 1, r = 2 * pr;
         if ((k & 1) == 0) {
-          e0 = fast_exp2(s_cur[r] - m_run);
-          e1 = fast_exp2(s_cur[r + 1] - m_run);
+          e0 = fast_exp2(__builtin_fmaf(s_cur[r], qscale, -m_run));
+          e1 = fast_exp2(__builtin_fmaf(s_cur[r + 1], qscale, -m_run));
         } else {
           const uint32_t pk = pack_bf16x2(e0, e1);
           // Pin the value to its slot: the compiler would otherwise sink the exponentials past
@@ -384,8 +373,8 @@ void prefill_kernel(const PrefillArgs<D> a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (wave_any(mxl > m_run + kSlack)) {
-      const float m_new = __builtin_fmaxf(m_run, pair_max(mxl));
+    if (wave_any(mxl * qscale > m_run + kSlack)) {
+      const float m_new = __builtin_fmaxf(m_run, pair_max(mxl) * qscale);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_pass[0] *= alpha;
