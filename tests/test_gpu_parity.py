@@ -119,6 +119,7 @@ SMALL_PREFILL = [
     (1, 300, 8, 1, 128, 64, 40, 1e4),       # 8:1 GQA (two head units per KV head)
     (1, 150, 3, 1, 64, 32, 20, 1e4),        # 3:1 GQA
     (1, 1100, 32, 8, 128, 300, 64, 1e6),    # Qwen3-8B heads, several query tiles, G = 4
+    (3, 333, 8, 2, 128, 128, 50, 1e6),      # batch 3, ragged, G = 3
 ]
 
 
@@ -315,6 +316,8 @@ SMALL_DECODE = [
     (1, 500, 2, 1, 128, 100, 1, 1e4, [200, 333]),                            # only the new token local
     (1, 400, 8, 2, 64, 64, 10000, 1e6, [257, 400]),                          # all local
     (1, 3000, 32, 8, 128, 1000, 128, 1e6, [2000, 2001, 2999, 3000]),         # Qwen3-8B heads
+    (16, 700, 8, 2, 128, 256, 64, 1e6, [700, 333]),                         # batch 16: 16 splits per sequence
+    (64, 300, 4, 1, 64, 64, 16, 1e4, [300, 77]),                            # batch 64: 4 splits per sequence
 ]
 
 
