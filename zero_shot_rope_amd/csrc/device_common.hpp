@@ -81,31 +81,6 @@ __device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, int delta, const u
   hi = ohi;
 }
 
-// Same rotation, with the results multiplied by `scale` before rounding to bf16.
-__device__ __forceinline__ void rotate8_scaled(u32x4& lo, u32x4& hi, int delta, const uint32_t* W, float scale) {
-  u32x4 olo, ohi;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    float x0 = bf16lo(lo[w]), x1 = bf16hi(lo[w]);
-    float y0 = bf16lo(hi[w]), y1 = bf16hi(hi[w]);
-    float s0, c0, s1, c1;
-    turns_sincos(phase_turns(delta, W[2 * w]), s0, c0);
-    turns_sincos(phase_turns(delta, W[2 * w + 1]), s1, c1);
-    olo[w] = pack_bf16x2((x0 * c0 - y0 * s0) * scale, (x1 * c1 - y1 * s1) * scale);
-    ohi[w] = pack_bf16x2((x0 * s0 + y0 * c0) * scale, (x1 * s1 + y1 * c1) * scale);
-  }
-  lo = olo;
-  hi = ohi;
-}
-
-// Eight bf16 values times `scale`, rounded back to bf16.
-__device__ __forceinline__ u32x4 scale8(u32x4 x, float scale) {
-  u32x4 r;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) r[w] = pack_bf16x2(bf16lo(x[w]) * scale, bf16hi(x[w]) * scale);
-  return r;
-}
-
 // acc + lo(pk) + hi(pk) for a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
 __device__ __forceinline__ float sum_bf16x2(uint32_t pk, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
