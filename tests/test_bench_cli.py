@@ -23,3 +23,11 @@ def test_traffic_reported_only_for_the_measured_sources(monkeypatch):
         assert bench.traffic(which) == rec["fetch_bytes"] + rec["write_bytes"]
         monkeypatch.setitem(bench.MEASURED_TRAFFIC, which, dict(rec, sources="0" * 16))
         assert bench.traffic(which) is None
+
+
+def test_committed_traffic_records_match_the_kernel_sources():
+    # The byte counters in bench.py were taken on the kernels as committed: a kernel edit without
+    # new counter runs makes the bench report traffic as null, and this test says so.
+    for which in ("prefill", "decode"):
+        assert bench.MEASURED_TRAFFIC[which]["sources"] == bench.sources_digest(which), which
+        assert bench.traffic(which) is not None
