@@ -664,6 +664,61 @@ def test_decode_varlen_dominant_key():
         lse_gate(lse[b:b + 1], ref_lse)
 
 
+# ---------------------------------------------------------------------------------------
+# Seeded random sweep: shapes, lengths, windows, pretrained windows and theta drawn from a
+# fixed generator (small sizes, every row compared), prefill in its three modes, a chunk of
+# it, and decode at a few lengths on the same tensors.
+# ---------------------------------------------------------------------------------------
+def _sweep_case(i):
+    rng = np.random.default_rng(9000 + i)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 2, 3, 4, 8]))
+    B = int(rng.choice([1, 1, 2]))
+    L = int(rng.integers(1, 420))
+    wp = int(rng.integers(1, 300))
+    w0 = int(rng.choice([0, 1, int(rng.integers(0, 200)), 10000]))
+    theta = float(rng.choice([1e4, 5e5, 1e6]))
+    return B, L, Hq, Hkv, D, wp, w0, theta
+
+
+SWEEP = [_sweep_case(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("i", range(len(SWEEP)), ids=[f"s{i}-B{c[0]}L{c[1]}H{c[2]}-{c[3]}D{c[4]}wp{c[5]}w{c[6]}"
+                                                     for i, c in enumerate(SWEEP)])
+def test_random_sweep(i):
+    B, L, Hq, Hkv, D, wp, w0, theta = SWEEP[i]
+    say(f"sweep {i}: B={B} L={L} Hq={Hq} Hkv={Hkv} D={D} wp={wp} w0={w0} theta={theta:g} G={group_size(L, wp)}")
+    bits = W.random_case(7000 + i, B, L, Hq, Hkv, D)
+    qf, kf, vf = f64(bits["q"]), f64(bits["k"]), f64(bits["v"])
+    ref_o, ref_lse = bifocal_attention(qf, kf, vf, w0=w0, w_pretrained=wp, theta=theta)
+    for mode in ("prerotated", "fused"):
+        o, lse = run_prefill(bits, w0, wp, theta, mode)
+        compare(o, ref_o, f"prefill {mode}")
+        assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
+    u_o, u_lse = three_pass_attention(qf, kf, vf, w0=w0, w_pretrained=wp, theta=theta)
+    o, lse = run_prefill(bits, w0, wp, theta, "unfused")
+    compare(o, u_o, "prefill unfused")
+    assert np.max(np.abs(lse - u_lse)) <= LSE_ABS
+    # The last rows as a chunk against the whole cache.
+    q_len = max(1, L // 3)
+    o, lse = run_chunk(bits["q"][:, L - q_len:], bits["k"], bits["v"], L - q_len, w0, wp, theta, "prerotated")
+    compare(o, ref_o[:, L - q_len:], "chunk")
+    # Decode of the last query at L and at a shorter length (its own G); the decode serves GQA
+    # groups of 1, 2 and 4 query heads per KV head and rejects the others before any launch.
+    if Hq // Hkv not in (1, 2, 4):
+        with pytest.raises(Z.BifocalError) as err:
+            run_decode(bits["q"][:, L - 1], bits["k"], bits["v"], L, w0, wp, theta)
+        assert err.value.status == -2
+        return
+    for Ld in sorted({L, max(1, (2 * L) // 3)}):
+        o, lse = run_decode(bits["q"][:, Ld - 1], bits["k"], bits["v"], Ld, w0, wp, theta)
+        rd_o, rd_lse = bifocal_decode(qf[:, Ld - 1], kf, vf, L=Ld, w0=w0, w_pretrained=wp, theta=theta)
+        compare(o, rd_o, f"decode L={Ld}")
+        assert np.max(np.abs(lse - rd_lse)) <= LSE_ABS
+
+
 def test_calls_are_deterministic():
     bits = W.random_case(5, 1, 600, 4, 1, 128)
     a, la = run_prefill(bits, 40, 128, 1e6)
