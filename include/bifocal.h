@@ -126,7 +126,7 @@ size_t bifocal_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, 
  * G is recomputed from this step's L (review page, Method: G follows the current length),
  * so a stream of calls crosses a change of G with no cache rewrite. Calls that share a
  * workspace must be ordered (same stream). head_dim must be 64 or 128, and
- * n_q_heads / n_kv_heads must be 1, 2 or 4.
+ * n_q_heads / n_kv_heads at most 16.
  * Returns BIFOCAL_OK or a negative bifocal_status. */
 int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                    int batch, int n_q_heads, int n_kv_heads, int head_dim,

@@ -123,7 +123,7 @@ def decode_call(lib, **kw):
     (dict(q=None), EINVAL), (dict(kc=None), EINVAL), (dict(vc=None), EINVAL), (dict(o=None), EINVAL),
     (dict(L=0), EINVAL), (dict(L=129), EINVAL), (dict(w0=-3), EINVAL), (dict(wp=0), EINVAL),
     (dict(theta=0.0), EINVAL), (dict(hq=7, hkv=2), EINVAL), (dict(batch=0), EINVAL),
-    (dict(d=80), EUNSUP), (dict(hq=16, hkv=2), EUNSUP), (dict(hq=6, hkv=2), EUNSUP),
+    (dict(d=80), EUNSUP), (dict(hq=34, hkv=2), EUNSUP), (dict(hq=64, hkv=2), EUNSUP),
     (dict(ws=None), EWS), (dict(wsb=0), EWS), (dict(wsb=16), EWS),
 ])
 def test_decode_rejects_before_any_hip_call(lib, kw, expect):
@@ -143,7 +143,7 @@ def step_call(lib, **kw):
     (dict(qr=None), EINVAL), (dict(kr=None), EINVAL), (dict(vn=None), EINVAL), (dict(kc=None), EINVAL),
     (dict(vc=None), EINVAL), (dict(o=None), EINVAL), (dict(L=0), EINVAL), (dict(L=129), EINVAL),
     (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL), (dict(theta=float("nan")), EINVAL), (dict(hq=6, hkv=4), EINVAL),
-    (dict(d=96), EUNSUP), (dict(hq=16, hkv=2), EUNSUP), (dict(cap=(1 << 30) + 1), EUNSUP), (dict(ws=None), EWS),
+    (dict(d=96), EUNSUP), (dict(hq=34, hkv=2), EUNSUP), (dict(cap=(1 << 30) + 1), EUNSUP), (dict(ws=None), EWS),
     (dict(wsb=0), EWS),
 ])
 def test_decode_step_rejects_before_any_hip_call(lib, kw, expect):
@@ -163,7 +163,7 @@ def varlen_call(lib, **kw):
 @pytest.mark.parametrize("kw,expect", [
     (dict(lens=None), EINVAL), (dict(q=None), EINVAL), (dict(max_len=0), EINVAL), (dict(max_len=129), EINVAL),
     (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL), (dict(theta=-2.0), EINVAL), (dict(batch=0), EINVAL),
-    (dict(d=80), EUNSUP), (dict(hq=16, hkv=2), EUNSUP), (dict(ws=None), EWS), (dict(wsb=16), EWS),
+    (dict(d=80), EUNSUP), (dict(hq=34, hkv=2), EUNSUP), (dict(ws=None), EWS), (dict(wsb=16), EWS),
 ])
 def test_decode_varlen_rejects_before_any_hip_call(lib, kw, expect):
     assert varlen_call(lib, **kw) == expect
@@ -261,7 +261,7 @@ def decode_unfused_call(lib, **kw):
     (dict(q=None), EINVAL), (dict(kc=None), EINVAL), (dict(vc=None), EINVAL), (dict(o=None), EINVAL),
     (dict(L=0), EINVAL), (dict(L=129), EINVAL), (dict(w0=-3), EINVAL), (dict(wp=0), EINVAL),
     (dict(theta=0.0), EINVAL), (dict(hq=7, hkv=2), EINVAL), (dict(batch=0), EINVAL),
-    (dict(d=80), EUNSUP), (dict(hq=16, hkv=2), EUNSUP), (dict(cap=(1 << 30) + 1), EUNSUP),
+    (dict(d=80), EUNSUP), (dict(hq=34, hkv=2), EUNSUP), (dict(cap=(1 << 30) + 1), EUNSUP),
     (dict(ws=None), EWS), (dict(wsb=1024), EWS),
 ])
 def test_decode_unfused_rejects_before_any_hip_call(lib, kw, expect):

@@ -202,8 +202,8 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
     return BIFOCAL_EINVAL;
   if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
   if (!supported_head_dim(head_dim)) return BIFOCAL_EUNSUPPORTED;
-  const int group = n_q_heads / n_kv_heads;
-  if (group != 1 && group != 2 && group != 4) return BIFOCAL_EUNSUPPORTED;
+  // The query heads of one KV head are the 16 columns of the decode kernel's MFMA tile.
+  if (n_q_heads / n_kv_heads > 16) return BIFOCAL_EUNSUPPORTED;
   if (cache_capacity > kMaxL || batch > 65535) return BIFOCAL_EUNSUPPORTED;  // grid z limit
   if (lens != nullptr && (long double)batch * n_q_heads * bifocal::decode_varlen_slots(batch, n_kv_heads) *
                                (head_dim + 2) * 4 >= 4.0e18L)

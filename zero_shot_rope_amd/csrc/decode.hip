@@ -3,8 +3,9 @@
 //   same keys, so the workgroup streams each position's contiguous 2 KB of K and of V.
 //   The correction angles depend only on the key position, so the workgroup computes one
 //   cos/sin table per block (32 keys x D/2 frequencies) into LDS and every head's wave rotates
-//   its keys with it. Score and output products run on v_mfma_f32_16x16x32_bf16: a KV head has
-//   at most 4 query heads, so 16 output columns waste less than 32 and halve the accumulator.
+//   its keys with it. Score and output products run on v_mfma_f32_16x16x32_bf16: the query heads
+//   of a KV head (up to 16) are its 16 columns; the usual groups of 4 to 8 waste less of 16
+//   columns than of 32, and the accumulator is half as large.
 //   K rows load straight into A-operand registers (two register sets, so the next block's keys
 //   are in flight for a whole block); V goes global->LDS by direct loads into a per-wave
 //   double-buffered swizzled tile read back transposed for O^T = V^T P^T. Local and remote
