@@ -120,6 +120,8 @@ SMALL_PREFILL = [
     (1, 150, 3, 1, 64, 32, 20, 1e4),        # 3:1 GQA
     (1, 1100, 32, 8, 128, 300, 64, 1e6),    # Qwen3-8B heads, several query tiles, G = 4
     (3, 333, 8, 2, 128, 128, 50, 1e6),      # batch 3, ragged, G = 3
+    (1, 200, 16, 1, 64, 50, 20, 1e4),       # GQA 16:1 (four head units per KV head)
+    (1, 150, 5, 1, 128, 40, 10, 1e6),       # GQA 5:1 (one head per unit, 256-row tiles)
 ]
 
 
