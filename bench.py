@@ -227,6 +227,7 @@ def main():
         vbytes = 4096.0 * sum(vl)
         varlen = {"what": f"one call, {len(vl)} sequences of lengths {vl} (G per sequence), Qwen3-8B heads",
                   "us_per_call": round(vms * 1e3, 2), "GB/s": round(vbytes / (vms * 1e-3) / 1e9, 1),
+                  "frac_of_hbm_peak": round(vbytes / (vms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                   "bytes_per_call": vbytes}
         decode["batched_varlen"] = varlen
         del vk, vv, vq, vo, vws
@@ -257,6 +258,7 @@ def main():
             "what": "512 steps, each new token raw: base RoPE of q and k at p, K/V rows appended, then the decode",
             "ms_per_512_steps": round(s_ms, 3), "us_per_step": round(s_ms * 1e3 / dcfg.steps, 2),
             "GB/s": round(sbytes / (s_ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(sbytes / (s_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "overhead_us_per_step": round((s_ms - dec_avg) * 1e3 / dcfg.steps, 2)}
         del nk, nv
 
@@ -282,6 +284,8 @@ def main():
         decode["unfused_three_pass"] = {
             "what": "512 steps, each: all cached keys rotated into a copy, three plain decode passes, LSE merge",
             "ms_per_512_steps": round(u_ms, 3), "us_per_step": round(u_ms * 1e3 / dcfg.steps, 2),
+            "GB/s_of_the_cache": round(total_bytes / (u_ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(total_bytes / (u_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "fused_over_unfused_throughput": round(u_ms / dec_avg, 3)}
         del uws
 
@@ -384,15 +388,19 @@ def main():
                      "kernel": "prefill_kernel<128, prerotated> (+ rotate_keys_kernel)", "flops_per_launch": flops},
         "prefill_mode": "keys rotated once into a workspace, then the fused attention kernel",
         "single_launch_mode": {"what": "no workspace: key rotation per staged tile inside the attention kernel",
-                               "ms": round(fused_ms, 3), "TFLOP/s": round(flops / (fused_ms * 1e-3) / 1e12, 2)},
+                               "ms": round(fused_ms, 3), "TFLOP/s": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+                               "frac_of_mfma_peak": round(flops / (fused_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "matched_control": {"what": "same kernel, w0 >= L (plain causal RoPE attention)",
                             "ms": round(ctrl_ms, 3), "TFLOP/s": round(ctrl_tflops, 2),
+                            "frac_of_mfma_peak": round(ctrl_tflops / PEAK_BF16_TFLOPS, 4),
                             "bifocal_over_control": round(ctrl_ms / pre_avg, 4)},
         "chunked_prefill": {"what": f"rows {cq0}..{pcfg.L - 1} (4096 queries) against the 128K cache, G from L",
                             "ms": round(chunk_ms, 3), "TFLOP/s": round(cflops / (chunk_ms * 1e-3) / 1e12, 2),
+                            "frac_of_mfma_peak": round(cflops / (chunk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                             "flops": cflops},
         "unfused_three_pass": {"what": "rotations into copies, three plain attention launches, LSE merge",
                                "ms": round(unfused_ms, 3), "TFLOP/s": round(flops / (unfused_ms * 1e-3) / 1e12, 2),
+                               "frac_of_mfma_peak": round(flops / (unfused_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                "fused_over_unfused_throughput": round(unfused_ms / pre_avg, 3),
                                "unfused_over_control_throughput": round(ctrl_ms / unfused_ms, 3)},
         "decode": decode,
