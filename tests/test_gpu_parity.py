@@ -323,6 +323,7 @@ SMALL_DECODE = [
     (1, 500, 16, 2, 128, 128, 50, 1e6, [500, 257]),                          # GQA 8:1
     (2, 300, 6, 2, 64, 64, 20, 1e4, [300, 100]),                             # GQA 3:1
     (1, 300, 16, 1, 128, 100, 30, 1e6, [300, 64]),                           # GQA 16:1, every MFMA column live
+    (300, 80, 4, 1, 64, 32, 8, 1e4, [80, 33]),                               # batch 300: one split per sequence
 ]
 
 
@@ -491,6 +492,7 @@ SMALL_VARLEN = [
     (300, 4, 1, 64, 64, 10, 1e4, [1 + (37 * i * i + 11 * i) % 300 for i in range(70)]),
     (4000, 8, 2, 128, 512, 64, 1e6, [4000] + [1] * 5 + [33] * 5),               # one long, many tiny
     (900, 16, 2, 128, 256, 64, 1e6, [900, 450, 3]),                              # GQA 8:1
+    (60, 4, 1, 64, 32, 8, 1e4, [1 + (13 * i) % 60 for i in range(300)]),         # 300 sequences, 5 scan rounds
 ]
 
 
