@@ -143,8 +143,9 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
  *            rotated by base RoPE at p (angle p * omega_k, half-split pairs) and the value as is
  *   o, lse, workspace (>= bifocal_decode_workspace_bytes(..., L)), stream: as bifocal_decode.
  * The output equals bifocal_decode(rope(q_raw, p), caches with row p written, ..., L). The
- * rotated query is staged in o before the reduce overwrites it, so o must not alias q_raw,
- * k_raw or v_new. All arguments are checked before anything is written; on an error return
+ * rotation and the cache write happen inside the split kernel, so the step is the decode's two
+ * launches; o is written only by the second, after every read of q_raw, k_raw and v_new, so it
+ * may alias them. All arguments are checked before anything is written; on an error return
  * the caches are untouched. Returns BIFOCAL_OK or a negative bifocal_status. */
 int bifocal_decode_step(const void* q_raw, const void* k_raw, const void* v_new, void* k_cache, void* v_cache,
                         void* o, float* lse, int batch, int n_q_heads, int n_kv_heads, int head_dim,

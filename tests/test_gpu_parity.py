@@ -441,6 +441,45 @@ def test_decode_step_sequence(case):
             assert np.array_equal(W.round_to_bf16_bits(o.astype(np.float32)), np.repeat(vn, group, axis=1))
 
 
+STALE_STEP = [
+    (2, 100, 4, 2, 128, 16, 20, 1e4, 38),    # p in the middle of a 32-key block; G = 3
+    (1, 200, 8, 1, 64, 40, 10, 1e6, 161),    # p at the first row of a block; GQA 8:1
+    (1, 96, 4, 4, 128, 128, 96, 1e4, 96),    # p at the last row; G = 1
+]
+
+
+@pytest.mark.parametrize("case", STALE_STEP, ids=[f"B{c[0]}H{c[2]}-{c[3]}D{c[4]}L{c[8]}" for c in STALE_STEP])
+def test_decode_step_ignores_stale_rows(case):
+    """Cache rows p and beyond hold NaN before the step (never-written memory): the step must take
+    the new key and value for row p and for every row it reads past p, and o may alias q_raw."""
+    B, cap, Hq, Hkv, D, wp, w0, theta, L = case
+    p = L - 1
+    say(f"decode step over stale rows {case}")
+    rng = np.random.default_rng(1000 + L)
+    kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    k_ref, v_ref = f64(kb), f64(vb)
+    kb[:, p:] = 0x7FC0
+    vb[:, p:] = 0x7FC0
+    qr = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    kr = W.round_to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+    vn = W.round_to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+    kc, vc = dev(kb), dev(vb)
+    o, lse = run_decode_step(qr, kr, vn, kc, vc, L, w0, wp, theta)
+    ref_o, ref_lse, _, _ = decode_step_from_raw(f64(qr), f64(kr), f64(vn), k_ref, v_ref, L=L, w0=w0,
+                                                w_pretrained=wp, theta=theta)
+    compare(o, ref_o, f"o L={L}")
+    assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
+    assert np.array_equal(bits_of(vc)[:, p], vn)
+    # The same step with the output written over the raw query: identical bits.
+    kc2, vc2 = dev(kb), dev(vb)
+    q_io = dev(qr)
+    Z.decode_step(q_io, dev(kr), dev(vn), kc2, vc2, L=L, w0=w0, w_pretrained=wp, rope_theta=theta, out=q_io)
+    torch.cuda.synchronize()
+    assert np.array_equal(q_io.float().cpu().numpy(), o), "o aliasing q_raw changed the result"
+    assert np.array_equal(bits_of(kc2), bits_of(kc)) and np.array_equal(bits_of(vc2), bits_of(vc))
+
+
 def test_decode_step_qwen3_8b_full_cache():
     cfg = W.QWEN3_8B_DECODE
     say(f"decode step {cfg.name} (full cache, raw new token)")

@@ -195,7 +195,8 @@ size_t bifocal_decode_varlen_workspace_bytes(int batch, int n_q_heads, int n_kv_
 static int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int batch,
                        int n_q_heads, int n_kv_heads, int head_dim, const int32_t* lens, int64_t L,
                        int64_t cache_capacity, int64_t w0, int64_t w_pretrained, double rope_theta, void* workspace,
-                       size_t workspace_bytes, void* stream, bool check_only = false) {
+                       size_t workspace_bytes, void* stream, bool check_only = false,
+                       const void* k_new = nullptr, const void* v_new = nullptr) {
   if (!q || !k_cache || !v_cache || !o) return BIFOCAL_EINVAL;
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
   if (L < 1 || cache_capacity < L || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta))
@@ -242,6 +243,8 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   p.chunk = s.chunk;  // unused with per-sequence lengths
   p.scale_log2 = scale_log2_for(head_dim);
   p.W = W;
+  p.k_new = k_new;
+  p.v_new = v_new;
   return map_hip(bifocal::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -362,34 +365,11 @@ int bifocal_decode_step(const void* q_raw, const void* k_raw, const void* v_new,
                         int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained, double rope_theta,
                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!q_raw || !k_raw || !v_new || !k_cache || !v_cache || !o) return BIFOCAL_EINVAL;
-  // All other checks are the decode's; run them before anything is written.
-  const int st = decode_impl(o, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, nullptr, L,
-                             cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes, nullptr,
-                             /*check_only=*/true);
-  if (st != BIFOCAL_OK) return st;
-  if ((long long)batch * (n_q_heads + n_kv_heads) * (head_dim / 16) > 0x7fffffffLL * 256)
-    return BIFOCAL_EUNSUPPORTED;  // grid x limit of the new-token kernel
-  uint32_t W[64];
-  phase_increments(head_dim, rope_theta, W);
-  bifocal::RopeAppendLaunch r;
-  r.q_raw = q_raw;
-  r.k_raw = k_raw;
-  r.v_new = v_new;
-  r.q_out = o;
-  r.k_cache = k_cache;
-  r.v_cache = v_cache;
-  r.batch = batch;
-  r.n_q_heads = n_q_heads;
-  r.n_kv_heads = n_kv_heads;
-  r.head_dim = head_dim;
-  r.p = static_cast<int>(L - 1);
-  r.capacity = static_cast<int>(cache_capacity);
-  r.W = W;
-  const int st2 = map_hip(bifocal::launch_rope_append(r, static_cast<hipStream_t>(stream)));
-  if (st2 != BIFOCAL_OK) return st2;
-  // The rotated query sits in o; the reduce overwrites it only after the split kernel read it.
-  return decode_impl(o, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, nullptr, L,
-                     cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream, false);
+  // One launch pair: the split kernel of the chunk that ends at L applies base RoPE at L - 1 to
+  // the query and the key and writes the key and the value into cache row L - 1.
+  return decode_impl(q_raw, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, nullptr, L,
+                     cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream, false, k_raw,
+                     v_new);
 }
 
 int bifocal_decode_unfused(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int batch,

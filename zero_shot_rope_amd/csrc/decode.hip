@@ -27,6 +27,13 @@ struct DecodeArgs {
   const uint16_t* kc;
   const uint16_t* vc;
   float* ws;
+  // Decode step on a raw new token (NULL otherwise): q holds the raw query, k_new / v_new the raw
+  // key and the value of position p = L - 1; the kernel applies base RoPE at p to the query and
+  // the key, uses them for key p and writes key and value into cache row p (kc_w / vc_w).
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* kc_w;
+  uint16_t* vc_w;
   const int32_t* lens;  // per-sequence lengths (device), or NULL: every sequence has length L
   int B;
   int Hq, Hkv, L, cap;  // L: the length, or with lens the maximum length
@@ -370,6 +377,29 @@ void decode_split_kernel(const DecodeArgs<D> a) {
   load_k(k_begin, ka);
   wait_vmcnt<NKR + NLD>();  // q is in; block 0 stays in flight
   mask_q(qs);
+  // Phase increments of this lane's pairs (frequencies 32c + 8lg + e), for the new token's RoPE:
+  // read at uniform indices (scalar loads of the kernel arguments) and picked by lg, so no vector
+  // load joins the in-order wait for the cache blocks in flight.
+  auto pair_w = [&](int c, uint32_t (&w)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w0 = a.W[32 * c + e], w1 = a.W[32 * c + 8 + e];
+      const uint32_t w2 = a.W[32 * c + 16 + e], w3 = a.W[32 * c + 24 + e];
+      w[e] = lg < 2 ? (lg == 0 ? w0 : w1) : (lg == 2 ? w2 : w3);
+    }
+  };
+  if (a.k_new != nullptr) {
+    // Raw query: base RoPE at p (the same fixed-point phase as the correction angles).
+#pragma unroll
+    for (int c = 0; c < NQC / 2; ++c) {
+      uint32_t w[8];
+      pair_w(c, w);
+      u32x4 lo = qs[c], hi = qs[c + NQC / 2];
+      rotate8(lo, hi, p, w);
+      qs[c] = lo;
+      qs[c + NQC / 2] = hi;
+    }
+  }
   if (need_table) fill_table(k_begin, B0);
   lds_barrier();
   // MORE: a block i+1 exists (always true except for the chunk's last block).
@@ -381,7 +411,52 @@ void decode_split_kernel(const DecodeArgs<D> a) {
       if (need_table) fill_table(blk + kDecBlock, nxt);
       wait_vmcnt<NKR + NLD>();  // block i's K and V are in
     } else {
+      // Decode step on a raw token: the chunk that ends at L holds key p = L - 1 in this, its last
+      // block, and is the only one that reads cache row p (chunks are multiples of the block).
+      // The raw key and value are loaded beside the block's last wait; after it, the key (rotated
+      // by base RoPE at p) replaces the K registers of row p and the value the V tile's row p,
+      // and both go to cache row p. Rows past p, which the loads clamp to row p, take the same
+      // key and value, so the masked keys see exactly the data of a cache that already held them.
+      const bool new_tok = a.k_new != nullptr && k_end == L;
+      const size_t new_row = ((size_t)b * a.Hkv + gl) * D;
+      u32x4 kn_raw[NQC], vn_raw;
+      if (new_tok) {
+#pragma unroll
+        for (int c = 0; c < NQC; ++c)
+          kn_raw[c] = *reinterpret_cast<const u32x4*>(a.k_new + new_row + 32 * c + 8 * lg);
+        vn_raw = *reinterpret_cast<const u32x4*>(a.v_new + new_row + 8 * (lane % CPR));
+      }
       wait_vmcnt<0>();
+      if (new_tok) {
+#pragma unroll
+        for (int c = 0; c < NQC / 2; ++c) {
+          uint32_t w[8];
+          pair_w(c, w);
+          rotate8(kn_raw[c], kn_raw[c + NQC / 2], p, w);
+        }
+        const int r_p = p - blk;
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+          for (int c = 0; c < NQC; ++c)
+            if (16 * kg + li >= r_p) kc[kg * NQC + c] = kn_raw[c];
+        uint16_t* vt = vtile(cur);
+#pragma unroll
+        for (int n = 0; n < NLD; ++n) {
+          const int row = RPI * n + lane / CPR;
+          if (row >= r_p)
+            *reinterpret_cast<u32x4*>(vt + (vwave + row * D + 8 * ((lane % CPR) ^ vswz<D>(row)))) = vn_raw;
+        }
+        if (head_live) {
+          const size_t cache_row = (((size_t)b * a.cap + p) * a.Hkv + g) * D;
+          if (li == (r_p & 15)) {
+#pragma unroll
+            for (int c = 0; c < NQC; ++c)
+              *reinterpret_cast<u32x4*>(a.kc_w + cache_row + 32 * c + 8 * lg) = kn_raw[c];
+          }
+          if (lane < CPR) *reinterpret_cast<u32x4*>(a.vc_w + cache_row + 8 * lane) = vn_raw;
+        }
+      }
     }
     compute(blk, kc, cur);
     lds_barrier();
@@ -532,6 +607,10 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
   a.kc = static_cast<const uint16_t*>(p.k_cache);
   a.vc = static_cast<const uint16_t*>(p.v_cache);
   a.ws = p.workspace;
+  a.k_new = static_cast<const uint16_t*>(p.k_new);
+  a.v_new = static_cast<const uint16_t*>(p.v_new);
+  a.kc_w = p.k_new ? static_cast<uint16_t*>(const_cast<void*>(p.k_cache)) : nullptr;
+  a.vc_w = p.k_new ? static_cast<uint16_t*>(const_cast<void*>(p.v_cache)) : nullptr;
   a.lens = p.lens;
   a.wp = p.w_pretrained;
   a.Hq = p.n_q_heads;
@@ -561,67 +640,6 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream) {
   if (p.head_dim == 128) return launch_decode_d<128>(p, stream);
   if (p.head_dim == 64) return launch_decode_d<64>(p, stream);
-  return hipErrorInvalidValue;
-}
-
-// New-token preparation for a decode step on raw (pre-RoPE) vectors: base RoPE at position p
-// (angle p * omega_k, the same exact fixed-point phase as the correction rotation) of the query
-// (into q_out) and of the key (into cache row p), and the value copied into cache row p. One
-// thread per 8 rotation pairs of one head row: the B * Hq query rows, then the B * Hkv key rows.
-template <int D>
-__global__ __launch_bounds__(256) void rope_append_kernel(const uint16_t* __restrict__ q_raw,
-                                                          const uint16_t* __restrict__ k_raw,
-                                                          const uint16_t* __restrict__ v_new, uint16_t* __restrict__ q_out,
-                                                          uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int B,
-                                                          int Hq, int Hkv, int p, int cap, const DecodeArgs<D> a) {
-  constexpr int HALF = D / 2, MCH = HALF / 8;
-  const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long nq = (long long)B * Hq * MCH, nk = (long long)B * Hkv * MCH;
-  if (u >= nq + nk) return;
-  const int m = (int)(u % MCH);
-  const uint16_t* src;
-  uint16_t* dst;
-  if (u < nq) {
-    const long long row = u / MCH;  // b * Hq + h
-    src = q_raw + (size_t)row * D;
-    dst = q_out + (size_t)row * D;
-  } else {
-    const long long row = (u - nq) / MCH;  // b * Hkv + g
-    const long long b = row / Hkv, g = row % Hkv;
-    const size_t cache_row = ((size_t)b * cap + p) * Hkv + g;
-    src = k_raw + (size_t)row * D;
-    dst = kc + cache_row * D;
-    const uint16_t* vs = v_new + (size_t)row * D;
-    uint16_t* vd = vc + cache_row * D;
-    *reinterpret_cast<u32x4*>(vd + 8 * m) = *reinterpret_cast<const u32x4*>(vs + 8 * m);
-    *reinterpret_cast<u32x4*>(vd + HALF + 8 * m) = *reinterpret_cast<const u32x4*>(vs + HALF + 8 * m);
-  }
-  u32x4 lo = *reinterpret_cast<const u32x4*>(src + 8 * m);
-  u32x4 hi = *reinterpret_cast<const u32x4*>(src + HALF + 8 * m);
-  uint32_t w[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) w[e] = a.W[8 * m + e];
-  rotate8(lo, hi, p, w);
-  *reinterpret_cast<u32x4*>(dst + 8 * m) = lo;
-  *reinterpret_cast<u32x4*>(dst + HALF + 8 * m) = hi;
-}
-
-template <int D>
-static hipError_t launch_rope_append_d(const RopeAppendLaunch& r, hipStream_t stream) {
-  DecodeArgs<D> a{};
-  for (int i = 0; i < D / 2; ++i) a.W[i] = r.W[i];
-  const long long units = (long long)r.batch * (r.n_q_heads + r.n_kv_heads) * (D / 16);
-  hipLaunchKernelGGL(rope_append_kernel<D>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(r.q_raw), static_cast<const uint16_t*>(r.k_raw),
-                     static_cast<const uint16_t*>(r.v_new), static_cast<uint16_t*>(r.q_out),
-                     static_cast<uint16_t*>(r.k_cache), static_cast<uint16_t*>(r.v_cache), r.batch, r.n_q_heads,
-                     r.n_kv_heads, r.p, r.capacity, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_rope_append(const RopeAppendLaunch& r, hipStream_t stream) {
-  if (r.head_dim == 128) return launch_rope_append_d<128>(r, stream);
-  if (r.head_dim == 64) return launch_rope_append_d<64>(r, stream);
   return hipErrorInvalidValue;
 }
 

@@ -41,19 +41,10 @@ struct DecodeLaunch {
   int n_splits, chunk;
   float scale_log2;
   const uint32_t* W;
-};
-
-// New token of a decode step: base RoPE at position p into q_out and cache row p, value copied.
-struct RopeAppendLaunch {
-  const void* q_raw;
-  const void* k_raw;
-  const void* v_new;
-  void* q_out;
-  void* k_cache;
-  void* v_cache;
-  int batch, n_q_heads, n_kv_heads, head_dim;
-  int p, capacity;
-  const uint32_t* W;
+  // Decode step on a raw new token (NULL otherwise): q is the raw query and k_new / v_new the raw
+  // key and value of position L - 1, which the split kernel rotates and writes into cache row L - 1.
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
 };
 
 // Rows rotated by their correction offsets into a separate buffer: dst[b][r][h] =
@@ -84,7 +75,6 @@ struct Merge3Launch {
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 hipError_t launch_rotate_rows(const RotateRowsLaunch& p, hipStream_t stream);
 hipError_t launch_merge3(const Merge3Launch& p, hipStream_t stream);
-hipError_t launch_rope_append(const RopeAppendLaunch& r, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& p, hipStream_t stream);
 size_t prefill_workspace_bytes(long long batch, long long L, int n_kv_heads, int head_dim);
 hipError_t launch_positions(int L, int G, int32_t* f_out, int32_t* G_out, hipStream_t stream);
