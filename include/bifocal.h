@@ -12,6 +12,9 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers (HIP), row-major, no padding.
+ *   - Alignment: bf16 tensors and workspaces 16 bytes, float32 / int32 arrays 4 bytes (every
+ *     hipMalloc or torch allocation is 256-byte aligned); a misaligned pointer returns
+ *     BIFOCAL_EINVAL.
  *   - Element type is bfloat16 (raw 16-bit storage) for Q, K, V, O; LSE is float32.
  *   - q and k are POST-base-RoPE: each vector is already rotated at its absolute position
  *     (the cache convention of the method: cached keys stay at their base positions and

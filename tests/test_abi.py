@@ -20,6 +20,11 @@ OK, EINVAL, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4
 FAKE = 0x1000  # never dereferenced: every call using it fails a host-side check first
 
 
+def odd_float_ptr(offset):
+    """A float* argument FAKE + offset (not 4-byte aligned for odd offsets below 4)."""
+    return ctypes.cast(ctypes.c_void_p(FAKE + offset), ctypes.POINTER(ctypes.c_float))
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(build_mod.LIB):
@@ -84,6 +89,8 @@ def prefill_call(lib, **kw):
     (dict(d=96), EUNSUP), (dict(d=256), EUNSUP), (dict(L=(1 << 30) + 1), EUNSUP),
     (dict(hq=1 << 17, hkv=1 << 17), EUNSUP),  # n_kv_heads * head_dim = 2^24: 32-bit tile offsets
     (dict(ws=FAKE, wsb=0), EWS), (dict(ws=FAKE, wsb=256 * 2 * 128 * 2 - 1), EWS),
+    (dict(q=FAKE + 2), EINVAL), (dict(k=FAKE + 8), EINVAL), (dict(v=FAKE + 4), EINVAL), (dict(o=FAKE + 2), EINVAL),
+    (dict(lse=odd_float_ptr(2)), EINVAL), (dict(ws=FAKE + 8, wsb=1 << 40), EINVAL),
 ])
 def test_prefill_rejects_before_any_hip_call(lib, kw, expect):
     assert prefill_call(lib, **kw) == expect
@@ -105,6 +112,7 @@ def chunk_call(lib, **kw):
     (dict(hq=6, hkv=4), EINVAL), (dict(batch=0), EINVAL), (dict(d=96), EUNSUP),
     (dict(cap=(1 << 30) + 1, q_off=0), EUNSUP),
     (dict(ws=FAKE, wsb=150 * 2 * 128 * 2 - 1), EWS),   # sized for L = q_off + q_len = 150
+    (dict(kc=FAKE + 2), EINVAL), (dict(vc=FAKE + 8), EINVAL), (dict(lse=odd_float_ptr(1)), EINVAL),
 ])
 def test_prefill_chunk_rejects_before_any_hip_call(lib, kw, expect):
     assert chunk_call(lib, **kw) == expect
@@ -125,6 +133,8 @@ def decode_call(lib, **kw):
     (dict(theta=0.0), EINVAL), (dict(hq=7, hkv=2), EINVAL), (dict(batch=0), EINVAL),
     (dict(d=80), EUNSUP), (dict(hq=34, hkv=2), EUNSUP), (dict(hq=64, hkv=2), EUNSUP),
     (dict(ws=None), EWS), (dict(wsb=0), EWS), (dict(wsb=16), EWS),
+    (dict(q=FAKE + 2), EINVAL), (dict(kc=FAKE + 8), EINVAL), (dict(vc=FAKE + 4), EINVAL), (dict(o=FAKE + 2), EINVAL),
+    (dict(lse=odd_float_ptr(2)), EINVAL), (dict(ws=FAKE + 8), EINVAL),
 ])
 def test_decode_rejects_before_any_hip_call(lib, kw, expect):
     assert decode_call(lib, **kw) == expect
@@ -144,7 +154,8 @@ def step_call(lib, **kw):
     (dict(vc=None), EINVAL), (dict(o=None), EINVAL), (dict(L=0), EINVAL), (dict(L=129), EINVAL),
     (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL), (dict(theta=float("nan")), EINVAL), (dict(hq=6, hkv=4), EINVAL),
     (dict(d=96), EUNSUP), (dict(hq=34, hkv=2), EUNSUP), (dict(cap=(1 << 30) + 1), EUNSUP), (dict(ws=None), EWS),
-    (dict(wsb=0), EWS),
+    (dict(wsb=0), EWS), (dict(qr=FAKE + 2), EINVAL), (dict(kr=FAKE + 2), EINVAL), (dict(vn=FAKE + 8), EINVAL),
+    (dict(kc=FAKE + 4), EINVAL),
 ])
 def test_decode_step_rejects_before_any_hip_call(lib, kw, expect):
     # Every rejection happens before the cache row is written (the fake pointers are never touched).
@@ -164,6 +175,7 @@ def varlen_call(lib, **kw):
     (dict(lens=None), EINVAL), (dict(q=None), EINVAL), (dict(max_len=0), EINVAL), (dict(max_len=129), EINVAL),
     (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL), (dict(theta=-2.0), EINVAL), (dict(batch=0), EINVAL),
     (dict(d=80), EUNSUP), (dict(hq=34, hkv=2), EUNSUP), (dict(ws=None), EWS), (dict(wsb=16), EWS),
+    (dict(lens=ctypes.cast(ctypes.c_void_p(FAKE + 2), ctypes.POINTER(ctypes.c_int32))), EINVAL), (dict(q=FAKE + 8), EINVAL),
 ])
 def test_decode_varlen_rejects_before_any_hip_call(lib, kw, expect):
     assert varlen_call(lib, **kw) == expect
@@ -201,6 +213,9 @@ def test_positions_rejects_bad_arguments(lib):
     assert lib.bifocal_positions(0, 4, p, p, None) == EINVAL
     assert lib.bifocal_positions(10, 0, p, p, None) == EINVAL
     assert lib.bifocal_positions(1 << 31, 4, p, p, None) == EINVAL
+    odd = ctypes.cast(ctypes.c_void_p(FAKE + 2), ctypes.POINTER(ctypes.c_int32))
+    assert lib.bifocal_positions(10, 4, odd, p, None) == EINVAL
+    assert lib.bifocal_positions(10, 4, p, odd, None) == EINVAL
 
 
 def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
@@ -230,7 +245,7 @@ def prefill_unfused_call(lib, **kw):
     (dict(q=None), EINVAL), (dict(k=None), EINVAL), (dict(v=None), EINVAL), (dict(o=None), EINVAL),
     (dict(batch=0), EINVAL), (dict(L=0), EINVAL), (dict(w0=-1), EINVAL), (dict(wp=0), EINVAL),
     (dict(theta=0.0), EINVAL), (dict(hq=6, hkv=4), EINVAL), (dict(d=96), EUNSUP), (dict(L=(1 << 30) + 1), EUNSUP),
-    (dict(ws=None), EWS), (dict(wsb=0), EWS),
+    (dict(ws=None), EWS), (dict(wsb=0), EWS), (dict(q=FAKE + 2), EINVAL), (dict(ws=FAKE + 4), EINVAL),
 ])
 def test_prefill_unfused_rejects_before_any_hip_call(lib, kw, expect):
     assert prefill_unfused_call(lib, **kw) == expect
@@ -262,7 +277,7 @@ def decode_unfused_call(lib, **kw):
     (dict(L=0), EINVAL), (dict(L=129), EINVAL), (dict(w0=-3), EINVAL), (dict(wp=0), EINVAL),
     (dict(theta=0.0), EINVAL), (dict(hq=7, hkv=2), EINVAL), (dict(batch=0), EINVAL),
     (dict(d=80), EUNSUP), (dict(hq=34, hkv=2), EUNSUP), (dict(cap=(1 << 30) + 1), EUNSUP),
-    (dict(ws=None), EWS), (dict(wsb=1024), EWS),
+    (dict(ws=None), EWS), (dict(wsb=1024), EWS), (dict(kc=FAKE + 2), EINVAL), (dict(ws=FAKE + 8), EINVAL),
 ])
 def test_decode_unfused_rejects_before_any_hip_call(lib, kw, expect):
     assert decode_unfused_call(lib, **kw) == expect

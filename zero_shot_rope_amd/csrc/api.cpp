@@ -43,6 +43,11 @@ bool sane_theta(double t) { return t > 0.0 && isfinite(t); }
 // row stride n_kv_heads * head_dim elements).
 bool kv_row_fits(int n_kv_heads, int head_dim) { return (long long)n_kv_heads * head_dim < (1LL << 24); }
 
+// Alignment the kernels' vector accesses assume: bf16 tensors and workspaces are read and
+// written in 16-byte units, float and int32 arrays in 4-byte units. NULL passes both checks.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace of the unfused three-pass forms: the remote query and key copies, the three pass
@@ -142,6 +147,8 @@ int bifocal_prefill(const void* q, const void* k, const void* v, void* o, float*
                     int64_t L, int64_t w0, int64_t w_pretrained, double rope_theta,
                     void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o) return BIFOCAL_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) || !aligned4(lse))
+    return BIFOCAL_EINVAL;
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
   if (L < 1 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
   if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
@@ -159,6 +166,9 @@ int bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cach
                           int64_t w0, int64_t w_pretrained, double rope_theta,
                           void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !o) return BIFOCAL_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace) ||
+      !aligned4(lse))
+    return BIFOCAL_EINVAL;
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
   if (q_len < 1 || q_offset < 0 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
   if (cache_capacity < 1 || q_offset > cache_capacity - q_len) return BIFOCAL_EINVAL;  // L <= capacity
@@ -198,6 +208,9 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
                        size_t workspace_bytes, void* stream, bool check_only = false,
                        const void* k_new = nullptr, const void* v_new = nullptr) {
   if (!q || !k_cache || !v_cache || !o) return BIFOCAL_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace) ||
+      !aligned4(lse) || !aligned4(lens) || !aligned16(k_new) || !aligned16(v_new))
+    return BIFOCAL_EINVAL;
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
   if (L < 1 || cache_capacity < L || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta))
     return BIFOCAL_EINVAL;
@@ -269,6 +282,8 @@ int bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* o
                             int n_q_heads, int n_kv_heads, int head_dim, int64_t L, int64_t w0, int64_t w_pretrained,
                             double rope_theta, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o) return BIFOCAL_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) || !aligned4(lse))
+    return BIFOCAL_EINVAL;
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1) return BIFOCAL_EINVAL;
   if (L < 1 || w0 < 0 || w_pretrained < 1 || !sane_theta(rope_theta)) return BIFOCAL_EINVAL;
   if (n_q_heads % n_kv_heads != 0) return BIFOCAL_EINVAL;
@@ -467,7 +482,7 @@ int bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cach
 }
 
 int bifocal_positions(int64_t L, int64_t w_pretrained, int32_t* f_out, int32_t* G_out, void* stream) {
-  if (!f_out || !G_out) return BIFOCAL_EINVAL;
+  if (!f_out || !G_out || !aligned4(f_out) || !aligned4(G_out)) return BIFOCAL_EINVAL;
   if (L < 1 || w_pretrained < 1 || L > 0x7fffffffLL) return BIFOCAL_EINVAL;
   const int64_t G = bifocal_group_size(L, w_pretrained);
   return map_hip(bifocal::launch_positions(static_cast<int>(L), static_cast<int>(G), f_out, G_out,

@@ -493,23 +493,25 @@ void decode_split_kernel(const DecodeArgs<D> a) {
   }
 }
 
-// Reduce: one workgroup of 256 threads per (query head, 32-wide slice of d, batch). Thread t
-// takes splits t, t+256, ... : it loads each one's (max, sum, 32 outputs) at once (a single load
-// round trip for up to 256 splits) and merges them by an online log-sum-exp. One shuffle tree
-// and LDS give the block max M; each thread writes its sum and outputs rescaled to M into LDS,
-// and two LDS stages (8 groups of 32 rows, then the 8 group sums) add them up.
+// Reduce: one workgroup of 256 threads per (query head, 32-wide slice of d, batch). Thread
+// (group g, dim c) takes dim c of splits g, g+8, g+16, ...: the 32 threads of a group read one
+// split's 32 outputs as one coalesced 128-byte row and its (max, sum) as a broadcast. Up to 32
+// splits per thread are loaded at once (one load round trip for up to 256 splits) and merged by
+// a log-sum-exp against their common max; the 8 group results are merged the same way through
+// LDS behind one barrier.
 constexpr int kRedThreads = 256;
 constexpr int kRedGroups = kRedThreads / 32;
+constexpr int kRedBatch = 32;  // splits per thread per load round
 
 template <int D>
 __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
                                                                     float* __restrict__ lse, int Hq, int n_splits,
                                                                     const int32_t* __restrict__ lens, int B, int maxL) {
-  __shared__ float s_m[kRedThreads / 64];
-  __shared__ float s_row[kRedThreads][33];  // per thread: 32 rescaled outputs, then the rescaled sum
-  __shared__ float s_grp[kRedGroups][33];
+  __shared__ float s_m[kRedGroups], s_l[kRedGroups];
+  __shared__ float s_acc[kRedGroups][32];
   const int head = blockIdx.x, slice = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
+  const int c = t & 31, grp = t >> 5;
   // n_splits is the slot stride; with per-sequence lengths this sequence has ceil(L_b / chunk).
   int n_have = n_splits;
   if (lens != nullptr) {
@@ -523,58 +525,54 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
     n_have = s_n;
   }
   const float* src = ws + ((size_t)b * Hq + head) * n_splits * (D + 2);
-  float m = kNegBig, l = 0.f, acc[32];
+  // Running (max, sum, output) of this thread's splits; absent splits weigh exp2(kNegBig - max).
+  float m = kNegBig, l = 0.f, acc = 0.f;
+  for (int s0 = grp; s0 < n_have; s0 += kRedGroups * kRedBatch) {
+    float ms[kRedBatch], ls[kRedBatch], os[kRedBatch];
 #pragma unroll
-  for (int d = 0; d < 32; ++d) acc[d] = 0.f;
-  for (int sp = t; sp < n_have; sp += kRedThreads) {
-    const float* ps = src + (size_t)sp * (D + 2);
-    const float ms = ps[0], ls = ps[1];
-    f32x4 v[8];
-    const f32x4* pv = reinterpret_cast<const f32x4*>(ps + 2 + 32 * slice);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = pv[q];
-    const float mn = fmaxf(m, ms);
-    const float a = fast_exp2(m - mn), w = fast_exp2(ms - mn);
-    m = mn;
-    l = l * a + w * ls;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * q + e] = acc[4 * q + e] * a + w * v[q][e];
-  }
-  float M = m;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) s_m[wave] = M;
-  __syncthreads();
-  M = s_m[0];
-#pragma unroll
-  for (int w = 1; w < kRedThreads / 64; ++w) M = fmaxf(M, s_m[w]);
-  const float f = fast_exp2(m - M);
-#pragma unroll
-  for (int d = 0; d < 32; ++d) s_row[t][d] = acc[d] * f;
-  s_row[t][32] = l * f;
-  __syncthreads();
-  {
-    // Thread (g, c): column c (32 = the sum) of rows 32g .. 32g+31.
-    const int g = t >> 5, c = t & 31;
-    float x = 0.f, y = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < 32; ++r) x += s_row[32 * g + r][c];
-    s_grp[g][c] = x;
-    if (c == 0) {
-#pragma unroll 8
-      for (int r = 0; r < 32; ++r) y += s_row[32 * g + r][32];
-      s_grp[g][32] = y;
+    for (int u = 0; u < kRedBatch; ++u) {
+      const int sp = s0 + kRedGroups * u;
+      const float* ps = src + (size_t)min(sp, n_have - 1) * (D + 2);
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(ps);  // rows are 8-byte aligned: D + 2 is even
+      ms[u] = ml[0];
+      ls[u] = ml[1];
+      os[u] = ps[2 + 32 * slice + c];
+      if (sp >= n_have) {
+        ms[u] = kNegBig;
+        ls[u] = 0.f;
+        os[u] = 0.f;
+      }
     }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < kRedBatch; ++u) mx = fmaxf(mx, ms[u]);
+    const float a = fast_exp2(m - mx);
+    acc *= a;
+    l *= a;
+#pragma unroll
+    for (int u = 0; u < kRedBatch; ++u) {
+      const float w = fast_exp2(ms[u] - mx);
+      acc = __builtin_fmaf(w, os[u], acc);
+      l = __builtin_fmaf(w, ls[u], l);
+    }
+    m = mx;
+  }
+  s_acc[grp][c] = acc;
+  if (c == 0) {
+    s_m[grp] = m;
+    s_l[grp] = l;
   }
   __syncthreads();
   if (t < 32) {
+    float M = s_m[0];
+#pragma unroll
+    for (int g = 1; g < kRedGroups; ++g) M = fmaxf(M, s_m[g]);
     float tot = 0.f, den = 0.f;
 #pragma unroll
     for (int g = 0; g < kRedGroups; ++g) {
-      tot += s_grp[g][t];
-      den += s_grp[g][32];
+      const float w = fast_exp2(s_m[g] - M);
+      tot = __builtin_fmaf(w, s_acc[g][t], tot);
+      den = __builtin_fmaf(w, s_l[g], den);
     }
     o[((size_t)b * Hq + head) * D + 32 * slice + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(tot / den));
     if (lse != nullptr && slice == 0 && t == 0) lse[(size_t)b * Hq + head] = (M + __log2f(den)) * 0.69314718055994531f;
