@@ -13,6 +13,9 @@
 //   output) of its chunk to the workspace.
 // Per-sequence lengths: one chunk length for the whole batch, chosen on the device from the
 //   lengths so that every chunk of every sequence fits one grid of about one workgroup per CU.
+// Decode step on a raw new token: every workgroup applies base RoPE at p = L - 1 to its raw
+//   query columns in registers; the workgroup whose chunk ends at L also takes the raw key and
+//   value of position p, uses them for row p, and writes them into cache row p.
 // Reduce kernel: merges the partials of all chunks by log-sum-exp and writes bf16 o / lse.
 #include <type_traits>
 
