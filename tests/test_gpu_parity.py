@@ -772,3 +772,46 @@ def test_calls_are_deterministic():
     d1, _ = run_decode(qd, bits["k"], bits["v"], 600, 40, 128, 1e6)
     d2, _ = run_decode(qd, bits["k"], bits["v"], 600, 40, 128, 1e6)
     assert np.array_equal(d1, d2)
+
+
+def test_concurrent_streams_and_host_threads():
+    """Two host threads, each on its own stream, run prefills and decodes at once: the library
+    keeps no state, so every result equals the same call made alone, bit for bit."""
+    import threading
+
+    bits = W.random_case(6, 1, 700, 8, 2, 128)
+    ref_p, ref_pl = run_prefill(bits, 50, 128, 1e6)
+    qd = bits["q"][:, 699]
+    ref_d, ref_dl = run_decode(qd, bits["k"], bits["v"], 700, 50, 128, 1e6)
+    q, k, v, q1 = dev(bits["q"]), dev(bits["k"]), dev(bits["v"]), dev(qd)
+    B, L, Hq, D = q.shape
+    results, errors = {}, []
+
+    def worker(name):
+        try:
+            s = torch.cuda.Stream()  # default priority
+            with torch.cuda.stream(s):
+                ws = torch.empty(Z.bifocal_prefill_workspace_bytes(B, 2, D, L), dtype=torch.uint8, device="cuda")
+                outs = []
+                for _ in range(4):
+                    o, lse = Z.prefill(q, k, v, w0=50, w_pretrained=128, rope_theta=1e6, want_lse=True, workspace=ws,
+                                       stream=s)
+                    od, ld = Z.decode(q1, k, v, L=700, w0=50, w_pretrained=128, rope_theta=1e6, want_lse=True, stream=s)
+                    outs.append((o, lse, od, ld))
+            s.synchronize()
+            results[name] = [(o.float().cpu().numpy(), lse.cpu().numpy(), od.float().cpu().numpy(), ld.cpu().numpy())
+                             for o, lse, od, ld in outs]
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(n,)) for n in ("a", "b")]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert set(results) == {"a", "b"}
+    for name, outs in results.items():
+        for o, lse, od, ld in outs:
+            assert np.array_equal(o, ref_p) and np.array_equal(lse, ref_pl), f"prefill on thread {name}"
+            assert np.array_equal(od, ref_d) and np.array_equal(ld, ref_dl), f"decode on thread {name}"
