@@ -25,7 +25,8 @@
  *   - Softmax scale is 1/sqrt(head_dim). LSE outputs are natural-log log-sum-exps.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
  *     The library allocates nothing, keeps no state between calls, never synchronises
- *     the host, and is safe to call from several host threads.
+ *     the host, and is safe to call from several host threads. A call only launches kernels
+ *     on `stream` (no memset, copy or allocation), so it can be captured into a HIP graph.
  *   - Every argument is validated on the host BEFORE any HIP call; a failed check
  *     returns a negative status and leaves device memory untouched. C++ exceptions never
  *     cross this boundary. A failed kernel launch returns BIFOCAL_EHIP.

@@ -815,3 +815,52 @@ def test_concurrent_streams_and_host_threads():
         for o, lse, od, ld in outs:
             assert np.array_equal(o, ref_p) and np.array_equal(lse, ref_pl), f"prefill on thread {name}"
             assert np.array_equal(od, ref_d) and np.array_equal(ld, ref_dl), f"decode on thread {name}"
+
+
+def test_graph_capture_replays_match_eager():
+    """The entry points only launch kernels (no allocation, memset or host synchronisation), so a
+    prefill, a decode and a decode step captured into one HIP graph replay to the eager results,
+    bit for bit, on every replay, with eager work in between."""
+    bits = W.random_case(8, 1, 640, 8, 2, 128)
+    q, k, v = dev(bits["q"]), dev(bits["k"]), dev(bits["v"])
+    B, L, Hq, D = q.shape
+    q1 = dev(bits["q"][:, L - 1])
+    rng = np.random.default_rng(81)
+    kr = dev(W.round_to_bf16_bits(rng.standard_normal((B, 2, D), dtype=np.float32)))
+    vn = dev(W.round_to_bf16_bits(rng.standard_normal((B, 2, D), dtype=np.float32)))
+    kc, vc = k.clone(), v.clone()  # the step writes row L - 1 of these
+    pws = torch.empty(Z.bifocal_prefill_workspace_bytes(B, 2, D, L), dtype=torch.uint8, device="cuda")
+    dws = torch.empty(Z.bifocal_decode_workspace_bytes(B, Hq, 2, D, L), dtype=torch.uint8, device="cuda")
+    sws = torch.empty_like(dws)
+    o_p, l_p = torch.empty_like(q), torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    o_d, l_d = torch.empty_like(q1), torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    o_s = torch.empty_like(q1)
+    kw = dict(w0=48, w_pretrained=128, rope_theta=1e6)
+
+    def calls():
+        Z.prefill(q, k, v, out=o_p, lse=l_p, workspace=pws, **kw)
+        Z.decode(q1, k, v, L=L, out=o_d, lse=l_d, workspace=dws, **kw)
+        Z.decode_step(q1, kr, vn, kc, vc, L=L, out=o_s, workspace=sws, **kw)
+
+    snap = lambda: [t.float().cpu().numpy().copy() for t in (o_p, l_p, o_d, l_d, o_s, kc, vc)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()  # eager reference on the capture stream (also warms up)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = snap()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        for t in (o_p, l_p, o_d, l_d, o_s):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snap()
+        for a, b, name in zip(got, ref, ("o_prefill", "lse_prefill", "o_decode", "lse_decode", "o_step", "k_cache",
+                                         "v_cache")):
+            assert np.array_equal(a, b), f"replay {rep}: {name} differs from the eager call"
+        _ = (q.float() * 2).sum().item()  # eager work between replays
