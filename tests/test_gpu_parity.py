@@ -864,3 +864,33 @@ def test_graph_capture_replays_match_eager():
                                          "v_cache")):
             assert np.array_equal(a, b), f"replay {rep}: {name} differs from the eager call"
         _ = (q.float() * 2).sum().item()  # eager work between replays
+
+
+def test_binding_refuses_wrong_outputs_and_workspaces():
+    """Caller-supplied outputs must have exactly the shape and dtype the kernels write, and a
+    workspace must be device memory; otherwise ValueError, and nothing is launched."""
+    bits = W.random_case(9, 1, 128, 4, 2, 128)
+    q, k, v = dev(bits["q"]), dev(bits["k"]), dev(bits["v"])
+    B, L, Hq, D = q.shape
+    kw = dict(w0=16, w_pretrained=64, rope_theta=1e4)
+    sentinel = torch.full((B, L - 1, Hq, D), 3.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="out must be"):
+        Z.prefill(q, k, v, out=sentinel, **kw)
+    with pytest.raises(ValueError, match="out must be"):
+        Z.prefill(q, k, v, out=torch.empty(q.shape, dtype=torch.float32, device="cuda"), **kw)
+    with pytest.raises(ValueError, match="lse must be"):
+        Z.prefill(q, k, v, lse=torch.empty((B, Hq, L - 1), dtype=torch.float32, device="cuda"), **kw)
+    with pytest.raises(ValueError, match="workspace must be"):
+        Z.prefill(q, k, v, workspace=torch.empty(1 << 20, dtype=torch.uint8), **kw)
+    q1 = q[:, L - 1].contiguous()
+    with pytest.raises(ValueError, match="out must be"):
+        Z.decode(q1, k, v, L=L, out=torch.empty((B, Hq + 1, D), dtype=torch.bfloat16, device="cuda"), **kw)
+    with pytest.raises(ValueError, match="lse must be"):
+        Z.decode(q1, k, v, L=L, lse=torch.empty((B, Hq), dtype=torch.float64, device="cuda"), **kw)
+    with pytest.raises(ValueError, match="workspace must be"):
+        Z.decode(q1, k, v, L=L, workspace=torch.empty(1 << 20, dtype=torch.uint8), **kw)
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 3.0)
+    o = Z.prefill(q, k, v, **kw)  # the same call with valid arguments runs
+    torch.cuda.synchronize()
+    assert o.shape == q.shape and torch.isfinite(o.float()).all()

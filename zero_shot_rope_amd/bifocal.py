@@ -250,13 +250,44 @@ def bifocal_positions(L, w_pretrained, f_out, G_out, stream=None) -> None:
 # ---------------------------------------------------------------------------------------
 # Tensor conveniences: shapes from the tensors, outputs allocated when not given
 # ---------------------------------------------------------------------------------------
-def _check(t, name, ndim):
+def _check(t, name, ndim, device=None):
     import torch
 
     if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous bfloat16 CUDA/HIP tensor")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def _outputs(out, lse, want_lse, out_shape, lse_shape, device):
+    """Allocate the outputs, or check the caller's: the kernels write exactly these shapes."""
+    import torch
+
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.bfloat16, device=device)
+    elif (not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16 or out.device != device
+          or not out.is_contiguous() or tuple(out.shape) != tuple(out_shape)):
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {tuple(out_shape)} on {device}")
+    if lse is None and want_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=device)
+    elif lse is not None and (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
+                              or lse.device != device or not lse.is_contiguous()
+                              or tuple(lse.shape) != tuple(lse_shape)):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {tuple(lse_shape)} on {device}")
+    return out, lse
+
+
+def _workspace(ws, need, device):
+    """The caller's workspace (any dtype; its size is checked by the library), or a new one."""
+    import torch
+
+    if ws is None:
+        return torch.empty(max(need, 4), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return ws
 
 
 def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_theta: float, out=None, lse=None,
@@ -269,17 +300,16 @@ def prefill(q, k, v, *, w0: int, w_pretrained: int, rope_theta: float, out=None,
     import torch
 
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, 4)
+        _check(t, n, 4, q.device)
     B, L, Hq, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[1] != L or k.shape[3] != D:
         raise ValueError("k/v shapes do not match q")
-    if out is None:
-        out = torch.empty_like(q)
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    out, lse = _outputs(out, lse, want_lse, q.shape, (B, Hq, L), q.device)
     if isinstance(workspace, str) and workspace == "auto":
         workspace = torch.empty(bifocal_prefill_workspace_bytes(B, k.shape[2], D, L), dtype=torch.uint8,
                                 device=q.device)
+    elif workspace is not None:
+        workspace = _workspace(workspace, 0, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     bifocal_prefill(q, k, v, out, lse, B, Hq, k.shape[2], D, L, w0, w_pretrained, rope_theta, workspace, ws_bytes,
                     _stream(stream, q.device))
@@ -297,19 +327,18 @@ def prefill_chunk(q, k_cache, v_cache, *, q_offset: int, w0: int, w_pretrained: 
     import torch
 
     _check(q, "q", 4)
-    _check(k_cache, "k_cache", 4)
-    _check(v_cache, "v_cache", 4)
+    _check(k_cache, "k_cache", 4, q.device)
+    _check(v_cache, "v_cache", 4, q.device)
     B, Lq, Hq, D = q.shape
     cap, Hkv = k_cache.shape[1], k_cache.shape[2]
     if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
         raise ValueError("cache shapes do not match q")
     L = int(q_offset) + Lq
-    if out is None:
-        out = torch.empty_like(q)
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    out, lse = _outputs(out, lse, want_lse, q.shape, (B, Hq, Lq), q.device)
     if isinstance(workspace, str) and workspace == "auto":
         workspace = torch.empty(bifocal_prefill_workspace_bytes(B, Hkv, D, L), dtype=torch.uint8, device=q.device)
+    elif workspace is not None:
+        workspace = _workspace(workspace, 0, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     bifocal_prefill_chunk(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, Lq, q_offset, cap, w0, w_pretrained,
                           rope_theta, workspace, ws_bytes, _stream(stream, q.device))
@@ -322,19 +351,14 @@ def decode(q, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, rope_thet
     import torch
 
     _check(q, "q", 3)
-    _check(k_cache, "k_cache", 4)
-    _check(v_cache, "v_cache", 4)
+    _check(k_cache, "k_cache", 4, q.device)
+    _check(v_cache, "v_cache", 4, q.device)
     B, Hq, D = q.shape
     cap, Hkv = k_cache.shape[1], k_cache.shape[2]
     if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
         raise ValueError("cache shapes do not match q")
-    need = bifocal_decode_workspace_bytes(B, Hq, Hkv, D, L)
-    if workspace is None:
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    workspace = _workspace(workspace, bifocal_decode_workspace_bytes(B, Hq, Hkv, D, L), q.device)
+    out, lse = _outputs(out, lse, want_lse, q.shape, (B, Hq), q.device)
     bifocal_decode(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained, rope_theta,
                    workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     return (out, lse) if (want_lse or lse is not None) else out
@@ -348,23 +372,18 @@ def decode_step(q_raw, k_raw, v_new, k_cache, v_cache, *, L: int, w0: int, w_pre
     import torch
 
     _check(q_raw, "q_raw", 3)
-    _check(k_raw, "k_raw", 3)
-    _check(v_new, "v_new", 3)
-    _check(k_cache, "k_cache", 4)
-    _check(v_cache, "v_cache", 4)
+    _check(k_raw, "k_raw", 3, q_raw.device)
+    _check(v_new, "v_new", 3, q_raw.device)
+    _check(k_cache, "k_cache", 4, q_raw.device)
+    _check(v_cache, "v_cache", 4, q_raw.device)
     B, Hq, D = q_raw.shape
     cap, Hkv = k_cache.shape[1], k_cache.shape[2]
     if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
         raise ValueError("cache shapes do not match q_raw")
     if k_raw.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D):
         raise ValueError("k_raw / v_new must be [batch, n_kv_heads, head_dim]")
-    need = bifocal_decode_workspace_bytes(B, Hq, Hkv, D, L)
-    if workspace is None:
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q_raw.device)
-    if out is None:
-        out = torch.empty_like(q_raw)
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q_raw.device)
+    workspace = _workspace(workspace, bifocal_decode_workspace_bytes(B, Hq, Hkv, D, L), q_raw.device)
+    out, lse = _outputs(out, lse, want_lse, q_raw.shape, (B, Hq), q_raw.device)
     bifocal_decode_step(q_raw, k_raw, v_new, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained,
                         rope_theta, workspace, workspace.numel() * workspace.element_size(),
                         _stream(stream, q_raw.device))
@@ -378,22 +397,17 @@ def decode_varlen(q, k_cache, v_cache, seq_lens, *, max_len: int, w0: int, w_pre
     import torch
 
     _check(q, "q", 3)
-    _check(k_cache, "k_cache", 4)
-    _check(v_cache, "v_cache", 4)
-    if not isinstance(seq_lens, torch.Tensor) or seq_lens.dtype != torch.int32 or not seq_lens.is_cuda \
+    _check(k_cache, "k_cache", 4, q.device)
+    _check(v_cache, "v_cache", 4, q.device)
+    if not isinstance(seq_lens, torch.Tensor) or seq_lens.dtype != torch.int32 or seq_lens.device != q.device \
             or not seq_lens.is_contiguous() or seq_lens.shape != (q.shape[0],):
-        raise ValueError("seq_lens must be a contiguous int32 CUDA/HIP tensor of shape [batch]")
+        raise ValueError("seq_lens must be a contiguous int32 tensor of shape [batch] on the inputs' device")
     B, Hq, D = q.shape
     cap, Hkv = k_cache.shape[1], k_cache.shape[2]
     if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
         raise ValueError("cache shapes do not match q")
-    need = bifocal_decode_varlen_workspace_bytes(B, Hq, Hkv, D, max_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    workspace = _workspace(workspace, bifocal_decode_varlen_workspace_bytes(B, Hq, Hkv, D, max_len), q.device)
+    out, lse = _outputs(out, lse, want_lse, q.shape, (B, Hq), q.device)
     bifocal_decode_varlen(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, seq_lens, max_len, cap, w0, w_pretrained,
                           rope_theta, workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     return (out, lse) if (want_lse or lse is not None) else out
@@ -406,17 +420,12 @@ def prefill_unfused(q, k, v, *, w0: int, w_pretrained: int, rope_theta: float, o
     import torch
 
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, 4)
+        _check(t, n, 4, q.device)
     B, L, Hq, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[1] != L or k.shape[3] != D:
         raise ValueError("k/v shapes do not match q")
-    if out is None:
-        out = torch.empty_like(q)
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = torch.empty(max(bifocal_prefill_unfused_workspace_bytes(B, Hq, k.shape[2], D, L), 4),
-                                dtype=torch.uint8, device=q.device)
+    out, lse = _outputs(out, lse, want_lse, q.shape, (B, Hq, L), q.device)
+    workspace = _workspace(workspace, bifocal_prefill_unfused_workspace_bytes(B, Hq, k.shape[2], D, L), q.device)
     bifocal_prefill_unfused(q, k, v, out, lse, B, Hq, k.shape[2], D, L, w0, w_pretrained, rope_theta, workspace,
                             workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     return (out, lse) if (want_lse or lse is not None) else out
@@ -428,19 +437,14 @@ def decode_unfused(q, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, r
     import torch
 
     _check(q, "q", 3)
-    _check(k_cache, "k_cache", 4)
-    _check(v_cache, "v_cache", 4)
+    _check(k_cache, "k_cache", 4, q.device)
+    _check(v_cache, "v_cache", 4, q.device)
     B, Hq, D = q.shape
     cap, Hkv = k_cache.shape[1], k_cache.shape[2]
     if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
         raise ValueError("cache shapes do not match q")
-    if workspace is None:
-        workspace = torch.empty(max(bifocal_decode_unfused_workspace_bytes(B, Hq, Hkv, D, cap), 4),
-                                dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    workspace = _workspace(workspace, bifocal_decode_unfused_workspace_bytes(B, Hq, Hkv, D, cap), q.device)
+    out, lse = _outputs(out, lse, want_lse, q.shape, (B, Hq), q.device)
     bifocal_decode_unfused(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained, rope_theta,
                            workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     return (out, lse) if (want_lse or lse is not None) else out
