@@ -721,7 +721,7 @@ def _sweep_case(i):
     rng = np.random.default_rng(9000 + i)
     D = int(rng.choice([64, 128]))
     Hkv = int(rng.choice([1, 2, 4]))
-    Hq = Hkv * int(rng.choice([1, 2, 3, 4, 8]))
+    Hq = Hkv * int(rng.choice([1, 2, 3, 4, 8, 16]))
     B = int(rng.choice([1, 1, 2]))
     L = int(rng.integers(1, 420))
     wp = int(rng.integers(1, 300))
@@ -730,7 +730,7 @@ def _sweep_case(i):
     return B, L, Hq, Hkv, D, wp, w0, theta
 
 
-SWEEP = [_sweep_case(i) for i in range(24)]
+SWEEP = [_sweep_case(i) for i in range(64)]
 
 
 @pytest.mark.parametrize("i", range(len(SWEEP)), ids=[f"s{i}-B{c[0]}L{c[1]}H{c[2]}-{c[3]}D{c[4]}wp{c[5]}w{c[6]}"
@@ -759,6 +759,24 @@ def test_random_sweep(i):
         rd_o, rd_lse = bifocal_decode(qf[:, Ld - 1], kf, vf, L=Ld, w0=w0, w_pretrained=wp, theta=theta)
         compare(o, rd_o, f"decode L={Ld}")
         assert np.max(np.abs(lse - rd_lse)) <= LSE_ABS
+    # One random length per sequence in one call, each against its own decode.
+    rng = np.random.default_rng(7100 + i)
+    lens = [int(x) for x in rng.integers(1, L + 1, size=B)]
+    o, lse = run_decode_varlen(bits["q"][:, L - 1], bits["k"], bits["v"], lens, L, w0, wp, theta)
+    for b, Lb in enumerate(lens):
+        rv_o, rv_lse = bifocal_decode(qf[b:b + 1, L - 1], kf[b:b + 1], vf[b:b + 1], L=Lb, w0=w0, w_pretrained=wp,
+                                      theta=theta)
+        compare(o[b:b + 1], rv_o, f"varlen b={b} L={Lb}")
+        assert np.max(np.abs(lse[b:b + 1] - rv_lse)) <= LSE_ABS
+    # A decode step at length L from raw new-token vectors (cache row L - 1 rewritten).
+    qr = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    kr = W.round_to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+    vn = W.round_to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+    o, lse = run_decode_step(qr, kr, vn, dev(bits["k"]), dev(bits["v"]), L, w0, wp, theta)
+    rs_o, rs_lse, _, _ = decode_step_from_raw(f64(qr), f64(kr), f64(vn), kf, vf, L=L, w0=w0, w_pretrained=wp,
+                                              theta=theta)
+    compare(o, rs_o, "decode step")
+    assert np.max(np.abs(lse - rs_lse)) <= LSE_ABS
 
 
 def test_calls_are_deterministic():
