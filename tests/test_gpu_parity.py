@@ -912,3 +912,42 @@ def test_binding_refuses_wrong_outputs_and_workspaces():
     o = Z.prefill(q, k, v, **kw)  # the same call with valid arguments runs
     torch.cuda.synchronize()
     assert o.shape == q.shape and torch.isfinite(o.float()).all()
+
+
+def test_long_context_one_million_keys():
+    """L = 2^20 + 4321 keys (G = 33 over a 32K window), one KV head of four query heads, D = 64:
+    32-bit offsets and split counts far past the 128K workload. Prefill (sampled rows) and its
+    last rows as a chunk, decode at L, and a per-sequence-length call, against the oracle."""
+    L, Hq, Hkv, D, wp, w0, theta = (1 << 20) + 4321, 4, 1, 64, 32768, 4096, 1e6
+    G = group_size(L, wp)
+    say(f"long context L={L} G={G}")
+    bits = W.random_case(1234, 1, L, Hq, Hkv, D)
+    o, lse = run_prefill(bits, w0, wp, theta)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = sample_rows(L, w0, G, seed=1235, n_random=8)
+    qv, kv, vv = (W.bf16_bits_to_float32(bits[x]) for x in ("q", "k", "v"))
+    ref_o, ref_lse = bifocal_attention(qv, kv, vv, w0=w0, w_pretrained=wp, theta=theta, rows=rows, block=16)
+    compare(o[:, rows], ref_o, "prefill o(sampled rows)")
+    assert np.max(np.abs(lse[:, :, rows] - ref_lse)) <= LSE_ABS
+    del o, lse
+    q_len = 3000
+    oc, lc = run_chunk(bits["q"][:, L - q_len:], bits["k"], bits["v"], L - q_len, w0, wp, theta)
+    tail = rows[rows >= L - q_len]
+    ref_t, ref_tl = bifocal_attention(qv, kv, vv, w0=w0, w_pretrained=wp, theta=theta, rows=tail, block=16)
+    compare(oc[:, tail - (L - q_len)], ref_t, "chunk o(sampled rows)")
+    assert np.max(np.abs(lc[:, :, tail - (L - q_len)] - ref_tl)) <= LSE_ABS
+    qd = bits["q"][:, L - 1]
+    od, ld = run_decode(qd, bits["k"], bits["v"], L, w0, wp, theta)
+    rd_o, rd_lse = bifocal_decode(qv[:, L - 1].astype(np.float64), kv, vv, L=L, w0=w0, w_pretrained=wp, theta=theta)
+    compare(od, rd_o, "decode")
+    assert np.max(np.abs(ld - rd_lse)) <= LSE_ABS
+    say("  per-sequence lengths [L, 300001]")
+    k2 = np.concatenate([bits["k"], bits["k"]])
+    v2 = np.concatenate([bits["v"], bits["v"]])
+    q2 = np.concatenate([qd, qd])
+    ov, lv = run_decode_varlen(q2, k2, v2, [L, 300001], L, w0, wp, theta)
+    compare(ov[:1], rd_o, "varlen b=0")
+    r1_o, r1_lse = bifocal_decode(qv[:, L - 1].astype(np.float64), kv[:, :300001], vv[:, :300001], L=300001, w0=w0,
+                                  w_pretrained=wp, theta=theta)
+    compare(ov[1:], r1_o, "varlen b=1")
+    assert np.max(np.abs(lv[0] - rd_lse[0])) <= LSE_ABS and np.max(np.abs(lv[1] - r1_lse[0])) <= LSE_ABS
