@@ -57,7 +57,7 @@ MEASURED_TRAFFIC = {
     # rotate_keys_kernel + prefill_kernel<128, prerotated> at the 128K Qwen3-8B shape.
     "prefill": {"sources": "2ae2ed0a334a2169", "fetch_bytes": 20316.76e6, "write_bytes": 1774.78e6},
     # decode_split_kernel + decode_reduce_kernel, mean over the 512 steps (L 98001..98512).
-    "decode": {"sources": "749281ad983bdafa", "fetch_bytes": 407.13e6, "write_bytes": 4.33e6},
+    "decode": {"sources": "f9984f8fd94a96fd", "fetch_bytes": 407.11e6, "write_bytes": 4.33e6},
 }
 # The files holding the measured kernels' device code and launch geometry.
 _KERNEL_SOURCES = {

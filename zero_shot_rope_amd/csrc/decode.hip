@@ -496,25 +496,26 @@ void decode_split_kernel(const DecodeArgs<D> a) {
   }
 }
 
-// Reduce: one workgroup of 256 threads per (query head, 32-wide slice of d, batch). Thread
-// (group g, dim c) takes dim c of splits g, g+8, g+16, ...: the 32 threads of a group read one
-// split's 32 outputs as one coalesced 128-byte row and its (max, sum) as a broadcast. Up to 32
+// Reduce: one workgroup of 256 threads per (query head, 16-wide slice of d, batch). Thread
+// (group g, dim c) takes dim c of splits g, g+16, g+32, ...: the 16 threads of a group read one
+// split's 16 outputs as one coalesced 64-byte row and its (max, sum) as a broadcast. Up to 16
 // splits per thread are loaded at once (one load round trip for up to 256 splits) and merged by
-// a log-sum-exp against their common max; the 8 group results are merged the same way through
-// LDS behind one barrier.
+// a log-sum-exp against their common max; the 16 group results are merged the same way through
+// LDS behind one barrier. (16-wide slices measured faster than 32- and 8-wide ones.)
 constexpr int kRedThreads = 256;
-constexpr int kRedGroups = kRedThreads / 32;
-constexpr int kRedBatch = 32;  // splits per thread per load round
+constexpr int kRedDims = 16;  // d per workgroup
+constexpr int kRedGroups = kRedThreads / kRedDims;
+constexpr int kRedBatch = 16;  // splits per thread per load round
 
 template <int D>
 __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
                                                                     float* __restrict__ lse, int Hq, int n_splits,
                                                                     const int32_t* __restrict__ lens, int B, int maxL) {
   __shared__ float s_m[kRedGroups], s_l[kRedGroups];
-  __shared__ float s_acc[kRedGroups][32];
+  __shared__ float s_acc[kRedGroups][kRedDims];
   const int head = blockIdx.x, slice = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int c = t & 31, grp = t >> 5;
+  const int c = t % kRedDims, grp = t / kRedDims;
   // n_splits is the slot stride; with per-sequence lengths this sequence has ceil(L_b / chunk).
   int n_have = n_splits;
   if (lens != nullptr) {
@@ -539,7 +540,7 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
       const f32x2 ml = *reinterpret_cast<const f32x2*>(ps);  // rows are 8-byte aligned: D + 2 is even
       ms[u] = ml[0];
       ls[u] = ml[1];
-      os[u] = ps[2 + 32 * slice + c];
+      os[u] = ps[2 + kRedDims * slice + c];
       if (sp >= n_have) {
         ms[u] = kNegBig;
         ls[u] = 0.f;
@@ -566,7 +567,7 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
     s_l[grp] = l;
   }
   __syncthreads();
-  if (t < 32) {
+  if (t < kRedDims) {
     float M = s_m[0];
 #pragma unroll
     for (int g = 1; g < kRedGroups; ++g) M = fmaxf(M, s_m[g]);
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
       tot = __builtin_fmaf(w, s_acc[g][t], tot);
       den = __builtin_fmaf(w, s_l[g], den);
     }
-    o[((size_t)b * Hq + head) * D + 32 * slice + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(tot / den));
+    o[((size_t)b * Hq + head) * D + kRedDims * slice + t] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(tot / den));
     if (lse != nullptr && slice == 0 && t == 0) lse[(size_t)b * Hq + head] = (M + __log2f(den)) * 0.69314718055994531f;
   }
 }
@@ -632,7 +633,7 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
   hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(kDecThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, D / 32, p.batch), dim3(kRedThreads), 0, stream,
+  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, D / kRedDims, p.batch), dim3(kRedThreads), 0, stream,
                      (const float*)p.workspace, static_cast<uint16_t*>(p.o), p.lse, p.n_q_heads, p.n_splits, p.lens,
                      p.batch, p.L);
   return hipGetLastError();
