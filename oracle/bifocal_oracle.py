@@ -39,6 +39,8 @@ decode == last prefill row.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional, Sequence
 
 import numpy as np
@@ -51,6 +53,7 @@ __all__ = [
     "rotate_pairs",
     "bifocal_attention",
     "bifocal_decode",
+    "bifocal_decode_steps",
     "three_pass_attention",
     "raw_bifocal_attention",
     "decode_step_from_raw",
@@ -127,15 +130,36 @@ def _check_shapes(q, k, v):
 # ---------------------------------------------------------------------------------------
 # Direct definition: per-pair score matrix, one causal softmax
 # ---------------------------------------------------------------------------------------
+def _run_jobs(fn, jobs, workers):
+    """Run fn(*job) for every job on a thread pool with one BLAS thread per worker.
+
+    Only the schedule is parallel: each job writes its own disjoint slice of the outputs."""
+    jobs = list(jobs)
+    if workers is None:
+        workers = min(16, os.cpu_count() or 1)
+    if workers <= 1 or len(jobs) <= 1:
+        for job in jobs:
+            fn(*job)
+        return
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            for f in [pool.submit(fn, *job) for job in jobs]:
+                f.result()
+
+
 def bifocal_attention(q, k, v, *, w0: int, w_pretrained: int, theta: float,
-                      rows: Optional[Sequence[int]] = None, block: int = 256):
+                      rows: Optional[Sequence[int]] = None, block: int = 64, workers: Optional[int] = None):
     """Dynamic bifocal attention from the per-pair definition.
 
     q: [B, L, Hq, D], k/v: [B, L, Hkv, D]; q and k post-base-RoPE at their absolute
     positions. Query head h reads KV head h // (Hq / Hkv).
-    `rows` optionally restricts the computed query rows (sorted or not); keys are always
+    `rows` optionally restricts the computed query rows (any order); keys are always
     0 .. i for row i, and G is always taken from the full length L.
     Only the requested rows (and the keys they reach) are converted to float64.
+    Rows are taken in ascending order in blocks of `block`, on `workers` threads (default:
+    the host's cores, at most 16) over (sequence, KV head, row block).
     Returns (O [B, R, Hq, D] float64, LSE [B, Hq, R] float64, natural log), R = len(rows).
     """
     B, L, Hq, Hkv, D = _check_shapes(q, k, v)
@@ -150,33 +174,46 @@ def bifocal_attention(q, k, v, *, w0: int, w_pretrained: int, theta: float,
     nk = int(rows.max()) + 1
     omega = rope_frequencies(D, theta)
     delta = correction_offsets(L, G).astype(np.float64)
-    kf = np.asarray(k[:, :nk], dtype=np.float64)
-    vf = np.asarray(v[:, :nk], dtype=np.float64)
-    k_rem = rotate_pairs(kf, (delta[:nk, None] * omega[None, :])[None, :, None, :])
     group = Hq // Hkv
     scale = 1.0 / math.sqrt(D)
+    order = np.argsort(rows, kind="stable")
+    srt = rows[order]
+    q_base = np.asarray(q[:, srt], dtype=np.float64)  # [B, R, Hq, D]
+    q_rem = rotate_pairs(q_base, (delta[srt][:, None] * omega[None, :])[None, :, None, :])
     out = np.zeros((B, rows.size, Hq, D), dtype=np.float64)
     lse = np.zeros((B, Hq, rows.size), dtype=np.float64)
-    for start in range(0, rows.size, block):
-        r = rows[start:start + block]
-        nkeys = int(r.max()) + 1
+    # Base keys, remote keys (corrected by Delta_j) and values of each KV head, contiguous.
+    kv_base, kv_rem, kv_val = {}, {}, {}
+
+    def prepare(b, kv):
+        kb = np.ascontiguousarray(k[b, :nk, kv], dtype=np.float64)
+        kv_base[b, kv] = kb
+        kv_rem[b, kv] = rotate_pairs(kb, delta[:nk, None] * omega[None, :])
+        kv_val[b, kv] = np.ascontiguousarray(v[b, :nk, kv], dtype=np.float64)
+
+    def row_block(b, kv, start):
+        sl = slice(start, start + block)
+        r = srt[sl]
+        nkeys = int(r[-1]) + 1
         j = np.arange(nkeys, dtype=np.int64)
         rel = r[:, None] - j[None, :]  # i - j
         local = (rel >= 0) & (rel < w0)
         remote = rel >= w0
-        qb = np.asarray(q[:, r], dtype=np.float64)  # [B, R, Hq, D]
-        qb_rem = rotate_pairs(qb, (delta[r][:, None] * omega[None, :])[None, :, None, :])
-        for b in range(B):
-            for h in range(Hq):
-                kv = h // group
-                s_base = (qb[b, :, h, :] @ kf[b, :nkeys, kv, :].T) * scale
-                s_rem = (qb_rem[b, :, h, :] @ k_rem[b, :nkeys, kv, :].T) * scale
-                s = np.where(local, s_base, np.where(remote, s_rem, -np.inf))
-                m = s.max(axis=1, keepdims=True)
-                p = np.exp(s - m)
-                l = p.sum(axis=1, keepdims=True)
-                out[b, start:start + r.size, h, :] = (p @ vf[b, :nkeys, kv, :]) / l
-                lse[b, h, start:start + r.size] = (m + np.log(l))[:, 0]
+        for h in range(Hq):
+            if h // group != kv:
+                continue
+            s_base = (q_base[b, sl, h] @ kv_base[b, kv][:nkeys].T) * scale
+            s_rem = (q_rem[b, sl, h] @ kv_rem[b, kv][:nkeys].T) * scale
+            s = np.where(local, s_base, np.where(remote, s_rem, -np.inf))
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            l = p.sum(axis=1, keepdims=True)
+            out[b, order[sl], h, :] = (p @ kv_val[b, kv][:nkeys]) / l
+            lse[b, h, order[sl]] = (m + np.log(l))[:, 0]
+
+    pairs = [(b, kv) for b in range(B) for kv in range(Hkv)]
+    _run_jobs(prepare, pairs, workers)
+    _run_jobs(row_block, [(b, kv, s0) for b, kv in pairs for s0 in range(0, rows.size, block)], workers)
     return out, lse
 
 
@@ -214,6 +251,74 @@ def bifocal_decode(q, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, t
             e = np.exp(s - m)
             out[b, h] = (e @ vb[b, :, kv, :]) / e.sum()
             lse[b, h] = m + math.log(e.sum())
+    return out, lse
+
+
+def bifocal_decode_steps(q_steps, k_cache, v_cache, *, lengths, w0: int, w_pretrained: int, theta: float,
+                         block: int = 64, workers: Optional[int] = None):
+    """A sequence of decode steps over one cache: step t's query q_steps[t], post-base-RoPE at
+    p_t = lengths[t] - 1, attends cached keys 0 .. p_t with its own group size
+    G_t = max(1, ceil(lengths[t] / w_pretrained)) ([review] Method: G follows the current
+    length). A key is local iff p_t - j < w0, else remote (aliased positions f(p_t), f(j)).
+
+    Each step is the decode of `bifocal_decode` at L = lengths[t]; here the steps that share a
+    group size share the corrected keys, and the steps of a block of `block` are scored as the
+    rows of one matrix, on `workers` threads over (group size, sequence, KV head, step block).
+    q_steps [T, B, Hq, D]; caches [B, Lcap, Hkv, D]. Returns (o [T, B, Hq, D], lse [T, B, Hq]).
+    """
+    q_steps = np.asarray(q_steps, dtype=np.float64)
+    T, B, Hq, D = q_steps.shape
+    lengths = np.asarray(lengths, dtype=np.int64).reshape(T)
+    Hkv = k_cache.shape[2]
+    if T == 0:
+        return np.zeros((0, B, Hq, D)), np.zeros((0, B, Hq))
+    if lengths.min() < 1 or lengths.max() > k_cache.shape[1]:
+        raise ValueError("L outside the cache")
+    if w0 < 0:
+        raise ValueError("w0 must be >= 0")
+    omega = rope_frequencies(D, theta)
+    group = Hq // Hkv
+    scale = 1.0 / math.sqrt(D)
+    G_of = np.array([group_size(int(L), w_pretrained) for L in lengths], dtype=np.int64)
+    nk = int(lengths.max())
+    out = np.zeros((T, B, Hq, D), dtype=np.float64)
+    lse = np.zeros((T, B, Hq), dtype=np.float64)
+    kv_base, kv_val = {}, {}
+
+    def prepare(b, kv):
+        kv_base[b, kv] = np.ascontiguousarray(k_cache[b, :nk, kv], dtype=np.float64)
+        kv_val[b, kv] = np.ascontiguousarray(v_cache[b, :nk, kv], dtype=np.float64)
+
+    def steps_of_group(G, b, kv):
+        st = np.nonzero(G_of == G)[0]
+        n_g = int(lengths[st].max())
+        delta = correction_offsets(n_g, G).astype(np.float64)
+        k_rem = rotate_pairs(kv_base[b, kv][:n_g], delta[:, None] * omega[None, :])
+        for s0 in range(0, st.size, block):
+            t = st[s0:s0 + block]
+            p = lengths[t] - 1  # query positions
+            nkeys = int(p.max()) + 1
+            j = np.arange(nkeys, dtype=np.int64)
+            rel = p[:, None] - j[None, :]  # p_t - j
+            local = (rel >= 0) & (rel < w0)
+            remote = rel >= w0
+            for h in range(Hq):
+                if h // group != kv:
+                    continue
+                qb = q_steps[t, b, h]  # [S, D]
+                qr = rotate_pairs(qb, delta[p][:, None] * omega[None, :])
+                s_base = (qb @ kv_base[b, kv][:nkeys].T) * scale
+                s_rem = (qr @ k_rem[:nkeys].T) * scale
+                s = np.where(local, s_base, np.where(remote, s_rem, -np.inf))
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                l = e.sum(axis=1, keepdims=True)
+                out[t, b, h] = (e @ kv_val[b, kv][:nkeys]) / l
+                lse[t, b, h] = (m + np.log(l))[:, 0]
+
+    pairs = [(b, kv) for b in range(B) for kv in range(Hkv)]
+    _run_jobs(prepare, pairs, workers)
+    _run_jobs(steps_of_group, [(int(G), b, kv) for G in np.unique(G_of) for b, kv in pairs], workers)
     return out, lse
 
 

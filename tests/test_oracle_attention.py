@@ -20,8 +20,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (bifocal_attention, bifocal_decode, decode_step_from_raw, group_size, raw_bifocal_attention,
-                    rope_frequencies, rotate_pairs, three_pass_attention)
+from oracle import (bifocal_attention, bifocal_decode, bifocal_decode_steps, decode_step_from_raw, group_size,
+                    raw_bifocal_attention, rope_frequencies, rotate_pairs, three_pass_attention)
 
 
 # --------------------------------------------------------------------------------------
@@ -275,3 +275,44 @@ def test_decode_step_from_raw_is_last_row_of_brute_force(case):
     # Rows other than p are untouched, and the inputs are not modified in place.
     keep = [r for r in range(cap) if r != p]
     assert np.array_equal(kc2[:, keep], kc[:, keep]) and np.array_equal(vc2[:, keep], vc[:, keep])
+
+
+# --------------------------------------------------------------------------------------
+# Decode steps over one cache (each step its own length and G)
+# --------------------------------------------------------------------------------------
+def test_decode_steps_match_brute_force_across_group_flips():
+    """Every step of a run whose length crosses two changes of G equals the last row of the
+    per-pair brute force at that length (raw query at p = L - 1, keys at base positions)."""
+    L_max, wp, w0, theta, D, Hq, Hkv = 38, 9, 4, 1e4, 8, 4, 2
+    qr, kr, v = _rand(90, 2, L_max, Hq, Hkv, D)
+    kc = rope_complex(kr, np.arange(L_max), theta)
+    lengths = [1, 2, 9, 10, 18, 19, 27, 28, 37, 38]  # G = 1 .. 5, w0 edge at L = 5
+    qs = np.stack([rope_complex(qr[:, L - 1:L], [L - 1], theta)[:, 0] for L in lengths])
+    o, lse = bifocal_decode_steps(qs, kc, v, lengths=lengths, w0=w0, w_pretrained=wp, theta=theta, block=3)
+    for t, L in enumerate(lengths):
+        want_o, want_lse = brute_force(qr[:, :L], kr[:, :L], v[:, :L], w0, wp, theta)
+        np.testing.assert_allclose(o[t], want_o[:, L - 1], rtol=0, atol=1e-11)
+        np.testing.assert_allclose(lse[t], want_lse[:, :, L - 1], rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("w0", [0, 1, 7, 1000])
+def test_decode_steps_equal_single_decodes(w0):
+    rng = np.random.default_rng(91 + w0)
+    B, cap, Hq, Hkv, D, wp, theta = 2, 300, 6, 2, 16, 64, 1e6
+    kc = rng.standard_normal((B, cap, Hkv, D))
+    vc = rng.standard_normal((B, cap, Hkv, D))
+    lengths = [300, 1, 64, 65, 128, 129, 200, 257]  # unordered, G from 1 to 5
+    qs = rng.standard_normal((len(lengths), B, Hq, D))
+    o, lse = bifocal_decode_steps(qs, kc, vc, lengths=lengths, w0=w0, w_pretrained=wp, theta=theta, block=2)
+    for t, L in enumerate(lengths):
+        o1, lse1 = bifocal_decode(qs[t], kc, vc, L=L, w0=w0, w_pretrained=wp, theta=theta)
+        np.testing.assert_allclose(o[t], o1, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[t], lse1, rtol=0, atol=1e-12)
+
+
+def test_row_blocks_and_workers_do_not_change_the_rows():
+    q, k, v = _rand(23, 2, 200, 4, 2, 16)
+    o1, l1 = bifocal_attention(q, k, v, w0=12, w_pretrained=48, theta=1e4, workers=1, block=200)
+    o2, l2 = bifocal_attention(q, k, v, w0=12, w_pretrained=48, theta=1e4, workers=4, block=7)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-13)

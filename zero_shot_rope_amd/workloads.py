@@ -105,6 +105,8 @@ QWEN3_4B_64K = {
 QWEN3_8B_128K = Prefill("qwen3_8b_L131072", 1, 32, 8, 128, 131072, 2048, 32768, 1.0e6, seed=4)
 # Single-batch decode, Qwen3-8B heads, 512 steps from 98001 keys (query position 98000).
 QWEN3_8B_DECODE = Decode("qwen3_8b_decode_98k", 1, 32, 8, 128, 98001, 512, 2048, 32768, 1.0e6, seed=5)
+# Single-batch decode at 128K: the same heads, 512 steps ending at 131072 keys (G = 4 throughout).
+QWEN3_8B_DECODE_128K = Decode("qwen3_8b_decode_128k", 1, 32, 8, 128, 131072 - 511, 512, 2048, 32768, 1.0e6, seed=8)
 
 
 def _draw(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
