@@ -32,13 +32,29 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def event_times(torch, stream, fn, n):
+    """Run fn() n times, each call bracketed by HIP events on `stream`; per-call milliseconds."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def spread(ms):
+    """Median, min and max of per-call milliseconds."""
+    return {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(float(np.min(ms)), 4),
+            "max_ms": round(float(np.max(ms)), 4), "calls": len(ms)}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time for the baseline sample")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode leg (profiling runs)")
     ap.add_argument("--decode-only", action="store_true", help="skip the prefill legs (profiling runs)")
     ap.add_argument("--main-only", action="store_true",
@@ -132,11 +148,11 @@ def main():
         Z.bifocal_prefill(q, k, v, o, None, pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim, pcfg.L, w0,
                           pcfg.w_pretrained, pcfg.rope_theta, ws, nb, sptr)
 
-    def decode_steps():
+    def decode_steps(w0=dcfg.w0):
         for t in range(dcfg.steps):
             L = dcfg.L_first + t
             Z.bifocal_decode(qs[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, L,
-                             dcfg.capacity, dcfg.w0, dcfg.w_pretrained, dcfg.rope_theta, ws, ws_bytes, sptr)
+                             dcfg.capacity, w0, dcfg.w_pretrained, dcfg.rope_theta, ws, ws_bytes, sptr)
 
     def step(ev):
         ev[0].record(stream)
@@ -198,11 +214,57 @@ def main():
                          "traffic_unit": "bytes per decode step (split + reduce kernels)"},
         }
 
-    # Batched decode with one length per sequence: 4 sequences of the Qwen3-8B heads, lengths
-    # 16K, 48K, 98512 and 128K in one call (each with its own G), caches of capacity 128K.
-    varlen = None
     side = not args.main_only
+    timing_calls = 10  # calls per side leg (per-call HIP events; median and spread reported)
+
     if do_decode and side:
+        # Matched decode control: the same 512 steps on the same cache with every key local
+        # (w0 >= L: plain causal decode, no correction rotation), interleaved pass by pass with the
+        # bifocal decode so both see the same clock.
+        bif, ctl = [], []
+        for _ in range(3):
+            bif += event_times(torch, stream, decode_steps, 1)
+            ctl += event_times(torch, stream, lambda: decode_steps(w0=dcfg.capacity), 1)
+        decode["matched_control"] = {
+            "what": "same 512 steps and cache, w0 >= L (plain causal decode), interleaved with the bifocal passes",
+            "bifocal_ms_per_512_steps": spread(bif), "control_ms_per_512_steps": spread(ctl),
+            "control_GB/s": round(total_bytes / (float(np.median(ctl)) * 1e-3) / 1e9, 1),
+            "bifocal_over_control": round(float(np.median(ctl)) / float(np.median(bif)), 4)}
+
+        # Single-sequence decode at 128K: 512 steps ending at 131072 keys (G = 4), with its control.
+        d128 = W.QWEN3_8B_DECODE_128K
+        gen = torch.Generator(device=dev).manual_seed(d128.seed)
+        shape = (d128.batch, d128.capacity, d128.n_kv_heads, d128.head_dim)
+        k128 = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+        v128 = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+        q128 = torch.randn((d128.steps, d128.batch, d128.n_q_heads, d128.head_dim), generator=gen,
+                           device=dev).to(torch.bfloat16)
+        ws128_b = Z.bifocal_decode_workspace_bytes(d128.batch, d128.n_q_heads, d128.n_kv_heads, d128.head_dim,
+                                                   d128.capacity)
+        ws128 = torch.empty(ws128_b, dtype=torch.uint8, device=dev)
+
+        def steps128(w0=d128.w0):
+            for t in range(d128.steps):
+                Z.bifocal_decode(q128[t], k128, v128, od, None, d128.batch, d128.n_q_heads, d128.n_kv_heads,
+                                 d128.head_dim, d128.L_first + t, d128.capacity, w0, d128.w_pretrained,
+                                 d128.rope_theta, ws128, ws128_b, sptr)
+        steps128()
+        b128, c128 = [], []
+        for _ in range(3):
+            b128 += event_times(torch, stream, steps128, 1)
+            c128 += event_times(torch, stream, lambda: steps128(w0=d128.capacity), 1)
+        bytes128 = float(sum(d128.bytes_per_step(d128.L_first + t) for t in range(d128.steps)))
+        g128 = bytes128 / (float(np.median(b128)) * 1e-3) / 1e9
+        decode["decode_128k"] = {
+            "what": f"one sequence, 512 steps from L = {d128.L_first} to {d128.capacity} (G = 4), Qwen3-8B heads",
+            "ms_per_512_steps": spread(b128), "us_per_step": round(float(np.median(b128)) * 1e3 / d128.steps, 2),
+            "GB/s": round(g128, 1), "frac_of_hbm_peak": round(g128 / PEAK_HBM_GBPS, 4),
+            "control_ms_per_512_steps": spread(c128),
+            "bifocal_over_control": round(float(np.median(c128)) / float(np.median(b128)), 4)}
+        del k128, v128, q128, ws128
+
+        # Batched decode with one length per sequence: 4 sequences of the Qwen3-8B heads, lengths
+        # 16K, 48K, 98512 and 128K in one call (each with its own G), caches of capacity 128K.
         vl = [16384, 49152, 98512, 131072]
         vcap = 131072
         gen = torch.Generator(device=dev).manual_seed(6)
@@ -213,46 +275,34 @@ def main():
         vlen = torch.tensor(vl, dtype=torch.int32, device=dev)
         vws_b = Z.bifocal_decode_varlen_workspace_bytes(len(vl), dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, vcap)
         vws = torch.empty(vws_b, dtype=torch.uint8, device=dev)
+
         def vcall():
             Z.bifocal_decode_varlen(vq, vk, vv, vo, None, len(vl), dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
                                     vlen, vcap, vcap, dcfg.w0, dcfg.w_pretrained, dcfg.rope_theta, vws, vws_b, sptr)
         vcall()
-        vev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
-        vev[0].record(stream)
-        for i in range(20):
-            vcall()
-            vev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        vms = float(np.median([vev[i].elapsed_time(vev[i + 1]) for i in range(20)]))
+        vms = float(np.median(event_times(torch, stream, vcall, 20)))
         vbytes = 4096.0 * sum(vl)
-        varlen = {"what": f"one call, {len(vl)} sequences of lengths {vl} (G per sequence), Qwen3-8B heads",
-                  "us_per_call": round(vms * 1e3, 2), "GB/s": round(vbytes / (vms * 1e-3) / 1e9, 1),
-                  "frac_of_hbm_peak": round(vbytes / (vms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                  "bytes_per_call": vbytes}
-        decode["batched_varlen"] = varlen
+        decode["batched_varlen"] = {
+            "what": f"one call, {len(vl)} sequences of lengths {vl} (G per sequence), Qwen3-8B heads",
+            "us_per_call": round(vms * 1e3, 2), "GB/s": round(vbytes / (vms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(vbytes / (vms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "bytes_per_call": vbytes}
         del vk, vv, vq, vo, vws
 
-    # The same 512 steps taking in each new token raw: base RoPE of its query and key at p = L - 1,
-    # key and value written into cache row p, then the decode (two launches per step).
-    if do_decode and side:
+        # The same 512 steps taking in each new token raw: base RoPE of its query and key at p = L - 1,
+        # key and value written into cache row p, then the decode (two launches per step).
         gen = torch.Generator(device=dev).manual_seed(7)
         nk = torch.randn((dcfg.steps, dcfg.batch, dcfg.n_kv_heads, dcfg.head_dim), generator=gen,
                          device=dev).to(torch.bfloat16)
         nv = torch.randn((dcfg.steps, dcfg.batch, dcfg.n_kv_heads, dcfg.head_dim), generator=gen,
                          device=dev).to(torch.bfloat16)
+
         def step_calls():
             for t in range(dcfg.steps):
                 Z.bifocal_decode_step(qs[t], nk[t], nv[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads,
                                       dcfg.n_kv_heads, dcfg.head_dim, dcfg.L_first + t, dcfg.capacity, dcfg.w0,
                                       dcfg.w_pretrained, dcfg.rope_theta, ws, ws_bytes, sptr)
         step_calls()
-        sev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for i in range(3):
-            sev[i].record(stream)
-            step_calls()
-        sev[3].record(stream)
-        torch.cuda.synchronize()
-        s_ms = float(np.median([sev[i].elapsed_time(sev[i + 1]) for i in range(3)]))
+        s_ms = float(np.median(event_times(torch, stream, step_calls, 3)))
         sbytes = total_bytes + dcfg.steps * dcfg.batch * (2 * dcfg.n_kv_heads + dcfg.n_q_heads) * dcfg.head_dim * 2
         decode["step_from_raw"] = {
             "what": "512 steps, each new token raw: base RoPE of q and k at p, K/V rows appended, then the decode",
@@ -262,25 +312,19 @@ def main():
             "overhead_us_per_step": round((s_ms - dec_avg) * 1e3 / dcfg.steps, 2)}
         del nk, nv
 
-    # The unfused three-pass decode (the pages' fusion ablation): per step the whole cache's keys
-    # are rotated into a copy, then three plain decode passes and a merge.
-    if do_decode and side:
+        # The unfused three-pass decode (the pages' fusion ablation): per step the whole cache's keys
+        # are rotated into a copy, then three plain decode passes and a merge.
         uws_b = Z.bifocal_decode_unfused_workspace_bytes(dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
                                                          dcfg.capacity)
         uws = torch.empty(uws_b, dtype=torch.uint8, device=dev)
+
         def unfused_steps():
             for t in range(dcfg.steps):
                 Z.bifocal_decode_unfused(qs[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads,
                                          dcfg.head_dim, dcfg.L_first + t, dcfg.capacity, dcfg.w0, dcfg.w_pretrained,
                                          dcfg.rope_theta, uws, uws_b, sptr)
         unfused_steps()
-        uev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        for i in range(2):
-            uev[i].record(stream)
-            unfused_steps()
-        uev[2].record(stream)
-        torch.cuda.synchronize()
-        u_ms = float(np.median([uev[i].elapsed_time(uev[i + 1]) for i in range(2)]))
+        u_ms = float(np.median(event_times(torch, stream, unfused_steps, 3)))
         decode["unfused_three_pass"] = {
             "what": "512 steps, each: all cached keys rotated into a copy, three plain decode passes, LSE merge",
             "ms_per_512_steps": round(u_ms, 3), "us_per_step": round(u_ms * 1e3 / dcfg.steps, 2),
@@ -295,70 +339,76 @@ def main():
         print(json.dumps({"decode": decode}), flush=True)
         return
 
-    # Matched control: the same kernel with every pair local (plain causal RoPE attention).
-    cev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    prefill(pcfg.L)
-    cev[0].record(stream)
-    prefill(pcfg.L)
-    cev[1].record(stream)
-    prefill(pcfg.L)
-    cev[2].record(stream)
-    torch.cuda.synchronize()
-    ctrl_ms = (cev[0].elapsed_time(cev[1]) + cev[1].elapsed_time(cev[2])) / 2.0
-    ctrl_tflops = flops / (ctrl_ms * 1e-3) / 1e12
-    # The single-launch mode (key rotation per staged tile, no workspace).
-    fev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    prefill(pcfg.w0, fused=True)
-    fev[0].record(stream)
-    prefill(pcfg.w0, fused=True)
-    fev[1].record(stream)
-    prefill(pcfg.w0, fused=True)
-    fev[2].record(stream)
-    torch.cuda.synchronize()
-    fused_ms = (fev[0].elapsed_time(fev[1]) + fev[1].elapsed_time(fev[2])) / 2.0
+    tfl = lambda ms: flops / (ms * 1e-3) / 1e12
+    legs = {}
+    if side:
+        # Matched control: the same kernel with every pair local (plain causal RoPE attention),
+        # interleaved call by call with the headline mode so both see the same clock.
+        head, ctrl = [], []
+        for _ in range(timing_calls):
+            head += event_times(torch, stream, lambda: prefill(pcfg.w0), 1)
+            ctrl += event_times(torch, stream, lambda: prefill(pcfg.L), 1)
+        ctrl_ms, head_ms = float(np.median(ctrl)), float(np.median(head))
+        legs["matched_control"] = {
+            "what": "same kernel, w0 >= L (plain causal RoPE attention), interleaved with headline calls",
+            "ms": round(ctrl_ms, 3), "TFLOP/s": round(tfl(ctrl_ms), 2),
+            "frac_of_mfma_peak": round(tfl(ctrl_ms) / PEAK_BF16_TFLOPS, 4),
+            "control_calls": spread(ctrl), "headline_calls": spread(head),
+            "bifocal_over_control": round(ctrl_ms / head_ms, 4)}
 
-    # Chunked prefill: the last 4096 query rows against the 128K cache (keys 0 .. L-1 already in
-    # it), G from L, keys rotated into the workspace first (as the headline mode).
-    cq0, cql = pcfg.L - 4096, 4096
-    qc = q[:, cq0:].contiguous()
-    oc = torch.empty_like(qc)
-    cflops = 4.0 * pcfg.n_q_heads * pcfg.head_dim * sum(range(cq0 + 1, pcfg.L + 1))
-    def chunk():
-        Z.bifocal_prefill_chunk(qc, k, v, oc, None, pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim, cql,
-                                cq0, pcfg.L, pcfg.w0, pcfg.w_pretrained, pcfg.rope_theta, pws, pws_bytes, sptr)
-    chunk()
-    chev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    for e in chev:
-        e.record(stream)
+        # The single-launch mode (key rotation per staged tile, no workspace).
+        fused = event_times(torch, stream, lambda: prefill(pcfg.w0, fused=True), timing_calls)
+        fused_ms = float(np.median(fused))
+        legs["single_launch_mode"] = {
+            "what": "no workspace: key rotation per staged tile inside the attention kernel",
+            "ms": round(fused_ms, 3), "TFLOP/s": round(tfl(fused_ms), 2),
+            "frac_of_mfma_peak": round(tfl(fused_ms) / PEAK_BF16_TFLOPS, 4), "calls": spread(fused),
+            "over_headline_time": round(fused_ms / head_ms, 4)}
+
+        # Chunked prefill: the last 4096 query rows against the 128K cache (keys 0 .. L-1 already in
+        # it), G from L, keys rotated into the workspace first (as the headline mode).
+        cq0, cql = pcfg.L - 4096, 4096
+        qc = q[:, cq0:].contiguous()
+        oc = torch.empty_like(qc)
+        cflops = 4.0 * pcfg.n_q_heads * pcfg.head_dim * sum(range(cq0 + 1, pcfg.L + 1))
+
+        def chunk():
+            Z.bifocal_prefill_chunk(qc, k, v, oc, None, pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim,
+                                    cql, cq0, pcfg.L, pcfg.w0, pcfg.w_pretrained, pcfg.rope_theta, pws, pws_bytes,
+                                    sptr)
         chunk()
-    end = torch.cuda.Event(enable_timing=True)
-    end.record(stream)
-    torch.cuda.synchronize()
-    chev.append(end)
-    chunk_ms = float(np.median([chev[i].elapsed_time(chev[i + 1]) for i in range(6)]))
-    del qc, oc
+        ch = event_times(torch, stream, chunk, timing_calls)
+        chunk_ms = float(np.median(ch))
+        legs["chunked_prefill"] = {
+            "what": f"rows {cq0}..{pcfg.L - 1} (4096 queries) against the 128K cache, G from L",
+            "ms": round(chunk_ms, 3), "TFLOP/s": round(cflops / (chunk_ms * 1e-3) / 1e12, 2),
+            "frac_of_mfma_peak": round(cflops / (chunk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "flops": cflops, "calls": spread(ch)}
+        del qc, oc
 
-    # The unfused three-pass prefill (the pages' fusion ablation): q and k rotated into copies,
-    # three plain attention launches (window/base, causal/remote, window/remote), LSE merge.
-    uws_b = Z.bifocal_prefill_unfused_workspace_bytes(pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim,
-                                                      pcfg.L)
-    uws = torch.empty(uws_b, dtype=torch.uint8, device=dev)
-    def unfused():
-        Z.bifocal_prefill_unfused(q, k, v, o, None, pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim, pcfg.L,
-                                  pcfg.w0, pcfg.w_pretrained, pcfg.rope_theta, uws, uws_b, sptr)
-    unfused()
-    uev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    for i in range(2):
-        uev[i].record(stream)
+        # The unfused three-pass prefill (the pages' fusion ablation): q and k rotated into copies,
+        # three plain attention launches (window/base, causal/remote, window/remote), LSE merge.
+        uws_b = Z.bifocal_prefill_unfused_workspace_bytes(pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads,
+                                                          pcfg.head_dim, pcfg.L)
+        uws = torch.empty(uws_b, dtype=torch.uint8, device=dev)
+
+        def unfused():
+            Z.bifocal_prefill_unfused(q, k, v, o, None, pcfg.batch, pcfg.n_q_heads, pcfg.n_kv_heads, pcfg.head_dim,
+                                      pcfg.L, pcfg.w0, pcfg.w_pretrained, pcfg.rope_theta, uws, uws_b, sptr)
         unfused()
-    uev[2].record(stream)
-    torch.cuda.synchronize()
-    unfused_ms = float(np.median([uev[i].elapsed_time(uev[i + 1]) for i in range(2)]))
-    del uws
+        un = event_times(torch, stream, unfused, timing_calls)
+        unfused_ms = float(np.median(un))
+        legs["unfused_three_pass"] = {
+            "what": "rotations into copies, three plain attention launches, LSE merge",
+            "ms": round(unfused_ms, 3), "TFLOP/s": round(tfl(unfused_ms), 2),
+            "frac_of_mfma_peak": round(tfl(unfused_ms) / PEAK_BF16_TFLOPS, 4), "calls": spread(un),
+            "fused_over_unfused_throughput": round(unfused_ms / head_ms, 3),
+            "unfused_over_control_throughput": round(ctrl_ms / unfused_ms, 3)}
+        del uws
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(pb, pcfg, args.cpu_seconds)
+        cpu = cpu_baseline(pb, pcfg, db if do_decode else None, dcfg)
 
     step_ms = wall * 1e3 / args.steps
     out = {
@@ -387,27 +437,13 @@ def main():
                      "traffic_unit": "bytes per prefill call (rotate + attention kernels)",
                      "kernel": "prefill_kernel<128, prerotated> (+ rotate_keys_kernel)", "flops_per_launch": flops},
         "prefill_mode": "keys rotated once into a workspace, then the fused attention kernel",
-        "single_launch_mode": {"what": "no workspace: key rotation per staged tile inside the attention kernel",
-                               "ms": round(fused_ms, 3), "TFLOP/s": round(flops / (fused_ms * 1e-3) / 1e12, 2),
-                               "frac_of_mfma_peak": round(flops / (fused_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
-        "matched_control": {"what": "same kernel, w0 >= L (plain causal RoPE attention)",
-                            "ms": round(ctrl_ms, 3), "TFLOP/s": round(ctrl_tflops, 2),
-                            "frac_of_mfma_peak": round(ctrl_tflops / PEAK_BF16_TFLOPS, 4),
-                            "bifocal_over_control": round(ctrl_ms / pre_avg, 4)},
-        "chunked_prefill": {"what": f"rows {cq0}..{pcfg.L - 1} (4096 queries) against the 128K cache, G from L",
-                            "ms": round(chunk_ms, 3), "TFLOP/s": round(cflops / (chunk_ms * 1e-3) / 1e12, 2),
-                            "frac_of_mfma_peak": round(cflops / (chunk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                            "flops": cflops},
-        "unfused_three_pass": {"what": "rotations into copies, three plain attention launches, LSE merge",
-                               "ms": round(unfused_ms, 3), "TFLOP/s": round(flops / (unfused_ms * 1e-3) / 1e12, 2),
-                               "frac_of_mfma_peak": round(flops / (unfused_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                               "fused_over_unfused_throughput": round(unfused_ms / pre_avg, 3),
-                               "unfused_over_control_throughput": round(ctrl_ms / unfused_ms, 3)},
+        **legs,
         "decode": decode,
         "context_from_pages": ("H100, other kernels and baselines, not comparable: fused prefill up to 1.39x "
                                "FlashAttention-2 and 0.83-0.88x FlashAttention-3 at 64K-128K; single-batch decode "
                                "within 4% of FlashAttention-2; unfused three-pass 0.29x; unfused decode 0.15-0.21x "
-                               "FlashAttention-3. Here: bifocal_over_control, fused_over_unfused_throughput."),
+                               "FlashAttention-3. Here: bifocal_over_control (prefill and decode), "
+                               "fused_over_unfused_throughput."),
         "cpu_baseline": cpu,
     }
     if args.copy_calibration:
@@ -425,42 +461,54 @@ def copy_calibration(torch, dev):
     del x, y
 
 
-def cpu_baseline(pb, pcfg, target_s):
-    """Time the fp64 oracle on a bounded sample of the same prefill workload (rank 0, N = 1)."""
-    from oracle import bifocal_attention
+def cpu_baseline(pb, pcfg, db, dcfg):
+    """Time the fp64 oracle on bounded samples of the same workloads (rank 0, N = 1): rows of the
+    128K prefill (the headline unit), decode steps of the 98K run, and every row of the in-window
+    8K prefill. The oracle runs on a thread pool (one BLAS thread per worker)."""
+    from oracle import bifocal_attention, bifocal_decode_steps
     from zero_shot_rope_amd import workloads as W
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    workers = min(16, os.cpu_count() or 1)
     qf = W.bf16_bits_to_float32(pb["q"])
     kf = W.bf16_bits_to_float32(pb["k"])
     vf = W.bf16_bits_to_float32(pb["v"])
     L = pcfg.L
-    # Rows from the end of the sequence (the longest causal rows), one block per timing unit.
-    rows_all = np.arange(L - 1, -1, -97)
-    done_rows = []
+    # Rows from the end down, every 64th (2048 rows over the whole length, all 32 heads).
+    rows = np.arange(L - 1, -1, -64)
     t0 = time.perf_counter()
-    n = 2
-    while True:
-        rows = rows_all[len(done_rows):len(done_rows) + n]
-        bifocal_attention(qf, kf, vf, w0=pcfg.w0, w_pretrained=pcfg.w_pretrained, theta=pcfg.rope_theta,
-                          rows=np.sort(rows), block=64)
-        done_rows.extend(rows.tolist())
-        el = time.perf_counter() - t0
-        if el >= target_s or len(done_rows) >= 256:
-            break
-        per_row = el / len(done_rows)
-        n = max(1, min(64, int((target_s - el) / per_row)))
+    bifocal_attention(qf, kf, vf, w0=pcfg.w0, w_pretrained=pcfg.w_pretrained, theta=pcfg.rope_theta, rows=rows,
+                      workers=workers)
     el = time.perf_counter() - t0
-    flop = sum(4.0 * pcfg.n_q_heads * pcfg.head_dim * (int(i) + 1) for i in done_rows)
-    log(f"cpu oracle: {len(done_rows)} rows in {el:.1f}s")
-    return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(done_rows)} query rows (every 97th from row {L - 1} down, all 32 heads) of the "
-                      f"128K prefill, fp64 numpy; {el:.1f} s including K/V conversion and rotation"}
+    flop = float(sum(4.0 * pcfg.n_q_heads * pcfg.head_dim * (int(i) + 1) for i in rows))
+    log(f"cpu oracle: {rows.size} prefill rows in {el:.1f}s")
+    out = {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": workers, "host_cpus": os.cpu_count(),
+           "kind": "oracle",
+           "sample": f"{rows.size} query rows (every 64th from row {L - 1} down, all 32 heads) of the 128K "
+                     f"prefill, fp64 numpy on {workers} threads; {el:.1f} s including the key rotation"}
+    del qf, kf, vf
+    if db is not None:
+        steps = np.arange(dcfg.steps)
+        t0 = time.perf_counter()
+        bifocal_decode_steps(W.bf16_bits_to_float32(db["q_steps"][steps]), W.bf16_bits_to_float32(db["k_cache"]),
+                             W.bf16_bits_to_float32(db["v_cache"]), lengths=dcfg.L_first + steps, w0=dcfg.w0,
+                             w_pretrained=dcfg.w_pretrained, theta=dcfg.rope_theta, workers=workers)
+        el = time.perf_counter() - t0
+        byts = float(sum(dcfg.bytes_per_step(dcfg.L_first + int(t)) for t in steps))
+        log(f"cpu oracle: {steps.size} decode steps in {el:.1f}s")
+        out["decode"] = {"value": round(byts / el / 1e9, 3), "unit": "GB/s",
+                         "sample": f"all {steps.size} decode steps (L {dcfg.L_first}..{dcfg.capacity}), algorithmic cache bytes; "
+                                   f"{el:.1f} s including the bf16 widening and key rotation"}
+    c2 = W.QWEN3_1_7B_8K
+    b2 = W.prefill_inputs(c2)
+    t0 = time.perf_counter()
+    bifocal_attention(W.bf16_bits_to_float32(b2["q"]), W.bf16_bits_to_float32(b2["k"]),
+                      W.bf16_bits_to_float32(b2["v"]), w0=c2.w0, w_pretrained=c2.w_pretrained, theta=c2.rope_theta,
+                      workers=workers)
+    el = time.perf_counter() - t0
+    log(f"cpu oracle: all {c2.L} rows of the in-window 8K prefill in {el:.1f}s")
+    out["in_window_8k"] = {"value": round(c2.flops() / el / 1e12, 6), "unit": "TFLOP/s",
+                           "sample": f"every row of the Qwen3-1.7B 8K prefill (16 heads); {el:.1f} s"}
+    return out
 
 
 if __name__ == "__main__":
