@@ -24,9 +24,11 @@
  *   - Query head h reads KV head h / (n_q_heads / n_kv_heads).
  *   - Softmax scale is 1/sqrt(head_dim). LSE outputs are natural-log log-sum-exps.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
- *     The library allocates nothing, keeps no state between calls, never synchronises
- *     the host, and is safe to call from several host threads. A call only launches kernels
- *     on `stream` (no memset, copy or allocation), so it can be captured into a HIP graph.
+ *     The library allocates nothing, never synchronises the host, and keeps no state between
+ *     calls apart from the static per-device scratch of bifocal_decode_noalloc (whose calls
+ *     must therefore not overlap on one device); every other entry point is safe to call from
+ *     several host threads at once. A call only launches kernels on `stream` (no memset, copy
+ *     or allocation), so it can be captured into a HIP graph.
  *   - Every argument is validated on the host BEFORE any HIP call; a failed check
  *     returns a negative status and leaves device memory untouched. C++ exceptions never
  *     cross this boundary. A failed kernel launch returns BIFOCAL_EHIP.
@@ -48,7 +50,8 @@ typedef enum {
   BIFOCAL_EINVAL = -1,       /* null pointer, non-positive size, bad w0/theta, head mismatch */
   BIFOCAL_EUNSUPPORTED = -2, /* valid arguments the kernels do not implement (head_dim, group) */
   BIFOCAL_EWORKSPACE = -3,   /* workspace missing (decode) or smaller than required */
-  BIFOCAL_EHIP = -4          /* a HIP runtime call or kernel launch failed */
+  BIFOCAL_EHIP = -4,         /* a HIP runtime call or kernel launch failed */
+  BIFOCAL_ESCRATCH = -5      /* bifocal_decode_noalloc: the shapes need more than its static scratch */
 } bifocal_status;
 
 /* Dynamic group size G = max(1, ceil(L / w_pretrained)) (review page, Method; gist.science
@@ -136,6 +139,27 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
                    int batch, int n_q_heads, int n_kv_heads, int head_dim,
                    int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
                    double rope_theta, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the static device scratch of bifocal_decode_noalloc (bytes, per device). */
+#define BIFOCAL_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* bifocal_decode without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation. The split
+ * partials go to a static device array of BIFOCAL_DECODE_NOALLOC_SCRATCH_BYTES that each device
+ * the library runs on holds until the process ends; the call allocates nothing and calls no
+ * allocating routine. Arguments, layouts, results and error checks are those of bifocal_decode;
+ * calls whose bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L) exceeds
+ * the scratch return BIFOCAL_ESCRATCH before any HIP call (16 MiB holds, for example, 32 query
+ * heads of head_dim 128 at any L for batch <= 256). The scratch used is the CURRENT device's:
+ * the tensors and `stream` must belong to the current device. Every call on a device shares
+ * that device's scratch, so calls that may overlap on one device (other streams, other host
+ * threads) race and must be ordered by the caller; nothing in the scratch needs to start at
+ * zero (every partial a call reads, it first writes). Returns BIFOCAL_OK or a negative
+ * bifocal_status. */
+int bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                           int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                           int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
+                           double rope_theta, void* stream);
 
 /* One decode step that also takes in the new token (review page, Method: keys are cached at
  * their base positions and never rewritten; gist.science summary, Methodologie section 2). The

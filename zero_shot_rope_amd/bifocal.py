@@ -24,6 +24,7 @@ EXPORTED_SYMBOLS = (
     "bifocal_prefill_chunk",
     "bifocal_decode_workspace_bytes",
     "bifocal_decode",
+    "bifocal_decode_noalloc",
     "bifocal_decode_step",
     "bifocal_decode_varlen_workspace_bytes",
     "bifocal_decode_varlen",
@@ -74,6 +75,9 @@ def load_library():
         lib.bifocal_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
                                        c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
         lib.bifocal_decode.restype = c_int
+        lib.bifocal_decode_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
+                                               c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp]
+        lib.bifocal_decode_noalloc.restype = c_int
         lib.bifocal_decode_step.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, fp, c_int, c_int, c_int, c_int,
                                             c_i64, c_i64, c_i64, c_i64, c_dbl, c_vp, c_sz, c_vp]
         lib.bifocal_decode_step.restype = c_int
@@ -179,6 +183,16 @@ def bifocal_decode(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, he
                             float(rope_theta), _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != 0:
         raise BifocalError(st, "bifocal_decode")
+
+
+def bifocal_decode_noalloc(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L, cache_capacity,
+                           w0, w_pretrained, rope_theta, stream=None) -> None:
+    lib = load_library()
+    st = lib.bifocal_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _fptr(lse), batch, n_q_heads,
+                                    n_kv_heads, head_dim, int(L), int(cache_capacity), int(w0), int(w_pretrained),
+                                    float(rope_theta), _stream(stream))
+    if st != 0:
+        raise BifocalError(st, "bifocal_decode_noalloc")
 
 
 def bifocal_decode_step(q_raw, k_raw, v_new, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, L,
@@ -361,6 +375,27 @@ def decode(q, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, rope_thet
     out, lse = _outputs(out, lse, want_lse, q.shape, (B, Hq), q.device)
     bifocal_decode(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained, rope_theta,
                    workspace, workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def decode_noalloc(q, k_cache, v_cache, *, L: int, w0: int, w_pretrained: int, rope_theta: float, out=None,
+                   lse=None, want_lse: bool = False, stream=None):
+    """`decode` through the entry point that allocates nothing: the split partials live in the
+    library's static scratch of the inputs' device (outputs are still allocated here when not
+    given). Calls that overlap on one device race on that scratch."""
+    import torch
+
+    _check(q, "q", 3)
+    _check(k_cache, "k_cache", 4, q.device)
+    _check(v_cache, "v_cache", 4, q.device)
+    B, Hq, D = q.shape
+    cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shapes do not match q")
+    out, lse = _outputs(out, lse, want_lse, q.shape, (B, Hq), q.device)
+    with torch.cuda.device(q.device):  # the library uses the current device's scratch
+        bifocal_decode_noalloc(q, k_cache, v_cache, out, lse, B, Hq, Hkv, D, L, cap, w0, w_pretrained, rope_theta,
+                               _stream(stream, q.device))
     return (out, lse) if (want_lse or lse is not None) else out
 
 

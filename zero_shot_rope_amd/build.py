@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbifocal.so")
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "unfused.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "unfused.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 

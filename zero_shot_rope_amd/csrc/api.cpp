@@ -97,6 +97,7 @@ const char* bifocal_status_string(int status) {
     case BIFOCAL_EUNSUPPORTED: return "unsupported configuration";
     case BIFOCAL_EWORKSPACE: return "workspace missing or too small";
     case BIFOCAL_EHIP: return "HIP runtime error";
+    case BIFOCAL_ESCRATCH: return "shapes need more than the static scratch of bifocal_decode_noalloc";
     default: return "unknown status";
   }
 }
@@ -267,6 +268,26 @@ int bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void
                    double rope_theta, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, nullptr, L,
                      cache_capacity, w0, w_pretrained, rope_theta, workspace, workspace_bytes, stream);
+}
+
+int bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                           int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                           int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
+                           double rope_theta, void* stream) {
+  // Every argument is checked before any HIP call (the workspace with a stand-in that is never
+  // used), then the size this call needs against the static scratch.
+  void* const stand_in = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+  const int st = decode_impl(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, nullptr, L,
+                             cache_capacity, w0, w_pretrained, rope_theta, stand_in, ~static_cast<size_t>(0),
+                             nullptr, /*check_only=*/true);
+  if (st != BIFOCAL_OK) return st;
+  const size_t need = bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L);
+  static_assert(bifocal::kDecodeScratchBytes == BIFOCAL_DECODE_NOALLOC_SCRATCH_BYTES, "scratch size mismatch");
+  if (need == 0 || need > bifocal::kDecodeScratchBytes) return BIFOCAL_ESCRATCH;
+  float* scratch = nullptr;
+  if (bifocal::decode_scratch(&scratch) != hipSuccess) return BIFOCAL_EHIP;
+  return decode_impl(q, k_cache, v_cache, o, lse, batch, n_q_heads, n_kv_heads, head_dim, nullptr, L,
+                     cache_capacity, w0, w_pretrained, rope_theta, scratch, bifocal::kDecodeScratchBytes, stream);
 }
 
 size_t bifocal_prefill_unfused_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim, int64_t L) {

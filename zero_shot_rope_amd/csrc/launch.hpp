@@ -89,4 +89,10 @@ DecodeSplit decode_split(long long L, int batch, int n_kv_heads);
 // Workgroups along x (and workspace slots per sequence) of a per-sequence-length decode.
 long long decode_varlen_slots(int batch, int n_kv_heads);
 
+// Static device scratch of bifocal_decode_noalloc (its size is the public maximum in bifocal.h).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+// Address of the current device's scratch (looked up once per device, then cached).
+hipError_t decode_scratch(float** out);
+
 }  // namespace bifocal
