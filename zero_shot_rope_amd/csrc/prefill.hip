@@ -115,7 +115,9 @@ void prefill_kernel(const PrefillArgs<D> a) {
   __shared__ uint32_t s_w[HALF];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform across the wave: from the scalar unit, everything derived from it
+  // alone (the head, the wave's rows, the per-tile routing) stays scalar too.
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
 
   // ---- work item: XCD-aware remap of the linear workgroup id ----
@@ -231,6 +233,10 @@ void prefill_kernel(const PrefillArgs<D> a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   float m_run = kNegBig;
+  // The largest raw (unscaled) half-tile max that needs no rescale: a score s with
+  // s * scale <= m_run + kSlack, kept in raw units so the check per half tile is one compare.
+  const float inv_qscale = 1.0f / qscale;
+  float m_lim = (kNegBig + kSlack) * inv_qscale;
   float l_pass[2] = {0.f, 0.f};  // [pass: 0 local (W_A), 1 remote (W_B - W_C)]
 
   // Operand offsets inside a tile (elements). K (A of S^T): row 32kb + col, chunk 2c + h.
@@ -342,7 +348,8 @@ void prefill_kernel(const PrefillArgs<D> a) {
     u32x4 op[NS];
 #pragma unroll
     for (int m = 0; m < AHEAD; ++m) op[m] = read_op(m);
-    float mxl = kMaskedMax, ps = 0.f, e0 = 0.f, e1 = 0.f;
+    // The row sums accumulate straight into this pass's weight sum.
+    float mxl = kMaskedMax, ps = l_pass[local_pass ? 0 : 1], e0 = 0.f, e1 = 0.f;
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
       __builtin_amdgcn_sched_barrier(0);
@@ -373,17 +380,21 @@ void prefill_kernel(const PrefillArgs<D> a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (wave_any(mxl * qscale > m_run + kSlack)) {
-      const float m_new = __builtin_fmaxf(m_run, pair_max(mxl) * qscale);
+    if (wave_any(mxl > m_lim)) {
+      const float mx_raw = pair_max(mxl);
+      const float m_new = __builtin_fmaxf(m_run, mx_raw * qscale);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
+      // At least the raw max just taken in, so the value that raised the max never raises it
+      // again through the rounding of the division.
+      m_lim = __builtin_fmaxf((m_new + kSlack) * inv_qscale, mx_raw);
       l_pass[0] *= alpha;
       l_pass[1] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      ps = exps(s_cur, pb_cur);
+      ps = l_pass[local_pass ? 0 : 1] + exps(s_cur, pb_cur);
     }
-    l_pass[local_pass ? 0 : 1] += ps;
+    l_pass[local_pass ? 0 : 1] = ps;
   };
 
   // One pass over n tiles kt = kt_first, kt_first-1, ... (tile t has keys j0(t) .. +63),
