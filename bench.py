@@ -73,7 +73,7 @@ MEASURED_TRAFFIC = {
     # rotate_keys_kernel + prefill_kernel<128, prerotated> at the 128K Qwen3-8B shape.
     "prefill": {"sources": "74673955f3c56af6", "fetch_bytes": 20104.01e6, "write_bytes": 1542.37e6},
     # decode_split_kernel + decode_reduce_kernel, mean over the 512 steps (L 98001..98512).
-    "decode": {"sources": "f9984f8fd94a96fd", "fetch_bytes": 407.11e6, "write_bytes": 4.33e6},
+    "decode": {"sources": "77822ba9bae08d86", "fetch_bytes": 407.07e6, "write_bytes": 4.33e6},
 }
 # The files holding the measured kernels' device code and launch geometry.
 _KERNEL_SOURCES = {
@@ -98,6 +98,20 @@ def traffic(which):
     if rec["sources"] is None or rec["sources"] != sources_digest(which):
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+LAYERS = 4  # distinct KV caches the decode legs cycle through, one per model layer
+
+
+def decode_layers(torch, dev, k0, v0, seed):
+    """LAYERS key and value caches of k0's shape: k0 and v0, then seeded standard-normal draws
+    (bf16), the distribution of the workload's own cache."""
+    gen = torch.Generator(device=dev).manual_seed(1000 + seed)
+    ks, vs = [k0], [v0]
+    for _ in range(LAYERS - 1):
+        ks.append(torch.randn(k0.shape, generator=gen, device=dev).to(torch.bfloat16))
+        vs.append(torch.randn(v0.shape, generator=gen, device=dev).to(torch.bfloat16))
+    return ks, vs
 
 
 def main():
@@ -133,12 +147,17 @@ def main():
         pws = torch.empty(pws_bytes, dtype=torch.uint8, device=dev)
     if do_decode:
         db = W.decode_inputs(dcfg)
-        kc, vc, qs = to_dev(db["k_cache"]), to_dev(db["v_cache"]), to_dev(db["q_steps"])
+        qs = to_dev(db["q_steps"])
+        # LAYERS caches of the workload's shape: the seeded workload cache, then seeded device draws
+        # of the same distribution. Step t reads cache t % LAYERS, as consecutive attention calls
+        # of a model read different layers' caches: no step finds the cache of the step before it
+        # in the 256 MB last-level cache.
+        kcs, vcs = decode_layers(torch, dev, to_dev(db["k_cache"]), to_dev(db["v_cache"]), dcfg.seed)
         od = torch.empty((dcfg.batch, dcfg.n_q_heads, dcfg.head_dim), dtype=torch.bfloat16, device=dev)
         ws_bytes = Z.bifocal_decode_workspace_bytes(dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
                                                     dcfg.capacity)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        log(f"decode cache {tuple(kc.shape)} ready")
+        log(f"decode caches {LAYERS} x {tuple(kcs[0].shape)} ready")
     sptr = stream.cuda_stream
 
     def prefill(w0, fused=False):
@@ -151,7 +170,7 @@ def main():
     def decode_steps(w0=dcfg.w0):
         for t in range(dcfg.steps):
             L = dcfg.L_first + t
-            Z.bifocal_decode(qs[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, L,
+            Z.bifocal_decode(qs[t], kcs[t % LAYERS], vcs[t % LAYERS], od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, L,
                              dcfg.capacity, w0, dcfg.w_pretrained, dcfg.rope_theta, ws, ws_bytes, sptr)
 
     def step(ev):
@@ -190,7 +209,7 @@ def main():
         ev[0].record(stream)
         for t in range(dcfg.steps):
             L = dcfg.L_first + t
-            Z.bifocal_decode(qs[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, L,
+            Z.bifocal_decode(qs[t], kcs[t % LAYERS], vcs[t % LAYERS], od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, L,
                              dcfg.capacity, dcfg.w0, dcfg.w_pretrained, dcfg.rope_theta, ws, ws_bytes, sptr)
             ev[t + 1].record(stream)
         torch.cuda.synchronize()
@@ -209,6 +228,7 @@ def main():
             "GBps_median_G4": round(float(np.median(gbps[flip])), 1),
             "GBps_min": round(float(gbps.min()), 1),
             "bytes_per_step": "4096 * L (K and V rows of 8 KV heads x 128 dims, bf16, read once)",
+            "layer_caches": f"{LAYERS} caches of this shape, step t reads cache t % {LAYERS}",
             "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic("decode"),
                          "traffic_unit": "bytes per decode step (split + reduce kernels)"},
@@ -235,8 +255,8 @@ def main():
         d128 = W.QWEN3_8B_DECODE_128K
         gen = torch.Generator(device=dev).manual_seed(d128.seed)
         shape = (d128.batch, d128.capacity, d128.n_kv_heads, d128.head_dim)
-        k128 = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
-        v128 = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+        k128 = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(LAYERS)]
+        v128 = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(LAYERS)]
         q128 = torch.randn((d128.steps, d128.batch, d128.n_q_heads, d128.head_dim), generator=gen,
                            device=dev).to(torch.bfloat16)
         ws128_b = Z.bifocal_decode_workspace_bytes(d128.batch, d128.n_q_heads, d128.n_kv_heads, d128.head_dim,
@@ -245,7 +265,7 @@ def main():
 
         def steps128(w0=d128.w0):
             for t in range(d128.steps):
-                Z.bifocal_decode(q128[t], k128, v128, od, None, d128.batch, d128.n_q_heads, d128.n_kv_heads,
+                Z.bifocal_decode(q128[t], k128[t % LAYERS], v128[t % LAYERS], od, None, d128.batch, d128.n_q_heads, d128.n_kv_heads,
                                  d128.head_dim, d128.L_first + t, d128.capacity, w0, d128.w_pretrained,
                                  d128.rope_theta, ws128, ws128_b, sptr)
         steps128()
@@ -256,7 +276,8 @@ def main():
         bytes128 = float(sum(d128.bytes_per_step(d128.L_first + t) for t in range(d128.steps)))
         g128 = bytes128 / (float(np.median(b128)) * 1e-3) / 1e9
         decode["decode_128k"] = {
-            "what": f"one sequence, 512 steps from L = {d128.L_first} to {d128.capacity} (G = 4), Qwen3-8B heads",
+            "what": f"one sequence, 512 steps from L = {d128.L_first} to {d128.capacity} (G = 4), Qwen3-8B heads, "
+                    f"step t on layer cache t % {LAYERS}",
             "ms_per_512_steps": spread(b128), "us_per_step": round(float(np.median(b128)) * 1e3 / d128.steps, 2),
             "GB/s": round(g128, 1), "frac_of_hbm_peak": round(g128 / PEAK_HBM_GBPS, 4),
             "control_ms_per_512_steps": spread(c128),
@@ -268,22 +289,28 @@ def main():
         vl = [16384, 49152, 98512, 131072]
         vcap = 131072
         gen = torch.Generator(device=dev).manual_seed(6)
-        vk = torch.randn((len(vl), vcap, dcfg.n_kv_heads, dcfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
-        vv = torch.randn((len(vl), vcap, dcfg.n_kv_heads, dcfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        vshape = (len(vl), vcap, dcfg.n_kv_heads, dcfg.head_dim)
+        vk = [torch.randn(vshape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(LAYERS)]
+        vv = [torch.randn(vshape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(LAYERS)]
         vq = torch.randn((len(vl), dcfg.n_q_heads, dcfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
         vo = torch.empty_like(vq)
         vlen = torch.tensor(vl, dtype=torch.int32, device=dev)
         vws_b = Z.bifocal_decode_varlen_workspace_bytes(len(vl), dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, vcap)
         vws = torch.empty(vws_b, dtype=torch.uint8, device=dev)
 
-        def vcall():
-            Z.bifocal_decode_varlen(vq, vk, vv, vo, None, len(vl), dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
+        vturn = [0]
+
+        def vcall():  # each call on the next layer's caches
+            lay = vturn[0] % LAYERS
+            vturn[0] += 1
+            Z.bifocal_decode_varlen(vq, vk[lay], vv[lay], vo, None, len(vl), dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
                                     vlen, vcap, vcap, dcfg.w0, dcfg.w_pretrained, dcfg.rope_theta, vws, vws_b, sptr)
         vcall()
         vms = float(np.median(event_times(torch, stream, vcall, 20)))
         vbytes = 4096.0 * sum(vl)
         decode["batched_varlen"] = {
-            "what": f"one call, {len(vl)} sequences of lengths {vl} (G per sequence), Qwen3-8B heads",
+            "what": f"one call, {len(vl)} sequences of lengths {vl} (G per sequence), Qwen3-8B heads, "
+                    f"successive calls on {LAYERS} layer caches in turn",
             "us_per_call": round(vms * 1e3, 2), "GB/s": round(vbytes / (vms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(vbytes / (vms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "bytes_per_call": vbytes}
         del vk, vv, vq, vo, vws
@@ -298,7 +325,7 @@ def main():
 
         def step_calls():
             for t in range(dcfg.steps):
-                Z.bifocal_decode_step(qs[t], nk[t], nv[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads,
+                Z.bifocal_decode_step(qs[t], nk[t], nv[t], kcs[t % LAYERS], vcs[t % LAYERS], od, None, dcfg.batch, dcfg.n_q_heads,
                                       dcfg.n_kv_heads, dcfg.head_dim, dcfg.L_first + t, dcfg.capacity, dcfg.w0,
                                       dcfg.w_pretrained, dcfg.rope_theta, ws, ws_bytes, sptr)
         step_calls()
@@ -320,7 +347,7 @@ def main():
 
         def unfused_steps():
             for t in range(dcfg.steps):
-                Z.bifocal_decode_unfused(qs[t], kc, vc, od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads,
+                Z.bifocal_decode_unfused(qs[t], kcs[t % LAYERS], vcs[t % LAYERS], od, None, dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads,
                                          dcfg.head_dim, dcfg.L_first + t, dcfg.capacity, dcfg.w0, dcfg.w_pretrained,
                                          dcfg.rope_theta, uws, uws_b, sptr)
         unfused_steps()
@@ -473,8 +500,8 @@ def cpu_baseline(pb, pcfg, db, dcfg):
     kf = W.bf16_bits_to_float32(pb["k"])
     vf = W.bf16_bits_to_float32(pb["v"])
     L = pcfg.L
-    # Rows from the end down, every 64th (2048 rows over the whole length, all 32 heads).
-    rows = np.arange(L - 1, -1, -64)
+    # Rows from the end down, every 32nd (4096 rows over the whole length, all 32 heads).
+    rows = np.arange(L - 1, -1, -32)
     t0 = time.perf_counter()
     bifocal_attention(qf, kf, vf, w0=pcfg.w0, w_pretrained=pcfg.w_pretrained, theta=pcfg.rope_theta, rows=rows,
                       workers=workers)
@@ -483,7 +510,7 @@ def cpu_baseline(pb, pcfg, db, dcfg):
     log(f"cpu oracle: {rows.size} prefill rows in {el:.1f}s")
     out = {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": workers, "host_cpus": os.cpu_count(),
            "kind": "oracle",
-           "sample": f"{rows.size} query rows (every 64th from row {L - 1} down, all 32 heads) of the 128K "
+           "sample": f"{rows.size} query rows (every 32nd from row {L - 1} down, all 32 heads) of the 128K "
                      f"prefill, fp64 numpy on {workers} threads; {el:.1f} s including the key rotation"}
     del qf, kf, vf
     if db is not None:

@@ -24,6 +24,13 @@
 
 namespace bifocal {
 
+// load_lds16 with the non-temporal hint (cache policy bit 1 of the operand: nt on gfx950), for
+// rows read once per launch: one pass over a cache larger than the last-level cache then reads
+// from HBM faster than with the default policy.
+__device__ __forceinline__ void load_lds16_nt(const void* g, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)lds_base, 16, 0, 2);
+}
+
 template <int D>
 struct DecodeArgs {
   const uint16_t* q;
@@ -221,6 +228,10 @@ void decode_split_kernel(const DecodeArgs<D> a) {
 
   // K block: lane (li, lg) holds keys blk + li (registers 0..NQC-1) and blk + 16 + li
   // (NQC..2NQC-1), d = 32c + 8lg .. +8. Rows past L are clamped to L-1; their scores are masked.
+  // Cache policies: each K load covers 64 bytes of 16 rows, half of each 128-byte line, and the
+  // next load (c + 1) the other half, so K keeps the default policy, under which the line
+  // fetched for the first half serves the second. V rows are read whole, 256 bytes per row
+  // per load, once per launch: V takes the non-temporal hint, which streams from HBM faster.
   auto load_k = [&](int blk, u32x4 (&kr)[NKR]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
@@ -237,7 +248,7 @@ void decode_split_kernel(const DecodeArgs<D> a) {
     for (int n = 0; n < NLD; ++n) {
       const int row = RPI * n + lane / CPR;
       const int j = min(blk + row, L - 1);
-      load_lds16(vbase + (size_t)j * row_stride + 8 * ((lane % CPR) ^ vswz<D>(row)),
+      load_lds16_nt(vbase + (size_t)j * row_stride + 8 * ((lane % CPR) ^ vswz<D>(row)),
                  vtile(buf) + (vwave + RPI * n * D));
     }
   };
