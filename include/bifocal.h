@@ -213,9 +213,10 @@ int bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cach
  * sliding window w0 on the remote vectors, then O = (W_A O_A + W_B O_B - W_C O_C) /
  * (W_A + W_B - W_C), W_X = exp(LSE_X - max(LSE_A, LSE_B)). These entry points run exactly that:
  * the remote vectors are rotated into the workspace, each pass is a separate plain-attention
- * launch writing bf16 O_X and fp32 LSE_X to the workspace, and a merge kernel writes o (and lse).
- * They exist to measure what the fusion saves; the results match the fused calls within bf16
- * rounding of the intermediate outputs. */
+ * launch writing O_X (fp32 in the prefill, bf16 in the decode, whose passes end in the decode's
+ * own reduce) and fp32 LSE_X to the workspace, and a merge kernel writes o (and lse). They exist
+ * to measure what the fusion saves; the results match the fused calls within the rounding of
+ * the materialised remote vectors q' and k' (and, in the decode, of the bf16 pass outputs). */
 
 /* Bytes of workspace for bifocal_prefill_unfused; 0 for invalid arguments. */
 size_t bifocal_prefill_unfused_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,

@@ -254,11 +254,11 @@ def test_prefill_unfused_rejects_before_any_hip_call(lib, kw, expect):
 def test_prefill_unfused_workspace_query(lib):
     assert lib.bifocal_prefill_unfused_workspace_bytes(0, 4, 2, 128, 256) == 0
     assert lib.bifocal_prefill_unfused_workspace_bytes(1, 4, 2, 96, 256) == 0
-    # q' + k' + three pass outputs (bf16) + three LSEs (fp32), each region 256-byte aligned.
+    # q' + k' + three pass outputs (fp32) + three LSEs (fp32), each region 256-byte aligned.
     B, Hq, Hkv, D, L = 2, 4, 2, 128, 300
     q, k, lse = B * L * Hq * D * 2, B * L * Hkv * D * 2, B * Hq * L * 4
     a = lambda x: (x + 255) // 256 * 256
-    assert lib.bifocal_prefill_unfused_workspace_bytes(B, Hq, Hkv, D, L) == 4 * a(q) + a(k) + 3 * a(lse)
+    assert lib.bifocal_prefill_unfused_workspace_bytes(B, Hq, Hkv, D, L) == a(q) + a(k) + 3 * a(2 * q) + 3 * a(lse)
     need = lib.bifocal_prefill_unfused_workspace_bytes(1, 4, 2, 128, 256)
     assert prefill_unfused_call(lib, wsb=need - 1) == EWS
 

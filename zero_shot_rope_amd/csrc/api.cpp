@@ -51,15 +51,17 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace of the unfused three-pass forms: the remote query and key copies, the three pass
-// outputs and their LSEs, and (decode) the split workspace the passes share.
+// outputs (o_bytes per element: 4 for the prefill's fp32 outputs, 2 for the decode's bf16) and
+// their LSEs, and (decode) the split workspace the passes share.
 struct UnfusedLayout {
   size_t qrem, krem, o[3], l[3], dws, total;
 };
 
 UnfusedLayout unfused_layout(size_t q_rows, size_t k_rows, int n_q_heads, int n_kv_heads, int head_dim,
-                             size_t lse_count, size_t dws_bytes) {
+                             size_t lse_count, size_t dws_bytes, size_t o_bytes) {
   UnfusedLayout u;
   const size_t qb = align256(q_rows * n_q_heads * head_dim * 2);
+  const size_t ob = align256(q_rows * n_q_heads * head_dim * o_bytes);
   const size_t kb = align256(k_rows * n_kv_heads * head_dim * 2);
   const size_t lb = align256(lse_count * 4);
   size_t at = 0;
@@ -69,7 +71,7 @@ UnfusedLayout unfused_layout(size_t q_rows, size_t k_rows, int n_q_heads, int n_
   at += kb;
   for (int x = 0; x < 3; ++x) {
     u.o[x] = at;
-    at += qb;
+    at += ob;
   }
   for (int x = 0; x < 3; ++x) {
     u.l[x] = at;
@@ -296,7 +298,7 @@ size_t bifocal_prefill_unfused_workspace_bytes(int batch, int n_q_heads, int n_k
   const long double elems = (long double)batch * (long double)L * n_q_heads * head_dim;
   if (elems >= 1.0e17L) return 0;
   const size_t rows = static_cast<size_t>(batch) * static_cast<size_t>(L);
-  return unfused_layout(rows, rows, n_q_heads, n_kv_heads, head_dim, rows * n_q_heads, 0).total;
+  return unfused_layout(rows, rows, n_q_heads, n_kv_heads, head_dim, rows * n_q_heads, 0, 4).total;
 }
 
 int bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
@@ -315,7 +317,7 @@ int bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* o
   if (!workspace || workspace_bytes < need) return BIFOCAL_EWORKSPACE;
 
   const size_t rows = static_cast<size_t>(batch) * static_cast<size_t>(L);
-  const UnfusedLayout u = unfused_layout(rows, rows, n_q_heads, n_kv_heads, head_dim, rows * n_q_heads, 0);
+  const UnfusedLayout u = unfused_layout(rows, rows, n_q_heads, n_kv_heads, head_dim, rows * n_q_heads, 0, 4);
   char* ws = static_cast<char*>(workspace);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t G = bifocal_group_size(L, w_pretrained);
@@ -343,7 +345,8 @@ int bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* o
   e = map_hip(bifocal::launch_rotate_rows(r, st));
   if (e != BIFOCAL_OK) return e;
 
-  // Three plain attention passes: A (window, base), B (causal, remote), C (window, remote).
+  // Three plain attention passes: A (window, base), B (causal, remote), C (window, remote), each
+  // writing its normalised output in fp32 so that the merge adds no bf16 rounding of its own.
   bifocal::PrefillLaunch p;
   p.krot = nullptr;
   p.v = v;
@@ -363,7 +366,8 @@ int bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* o
     if (pw[x] == 0) continue;  // w0 = 0: passes A and C hold no pair
     p.q = pq[x];
     p.k = pk[x];
-    p.o = ws + u.o[x];
+    p.o = nullptr;
+    p.o32 = reinterpret_cast<float*>(ws + u.o[x]);
     p.lse = reinterpret_cast<float*>(ws + u.l[x]);
     p.w0 = pw[x];
     e = map_hip(bifocal::launch_prefill(p, st));
@@ -384,6 +388,7 @@ int bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* o
   m.n_q_heads = n_q_heads;
   m.head_dim = head_dim;
   m.has_window = w > 0;
+  m.f32_in = true;
   return map_hip(bifocal::launch_merge3(m, st));
 }
 
@@ -393,7 +398,7 @@ size_t bifocal_decode_unfused_workspace_bytes(int batch, int n_q_heads, int n_kv
   if (dws == 0 || cache_capacity > kMaxL) return 0;
   const size_t b = static_cast<size_t>(batch);
   return unfused_layout(b, b * static_cast<size_t>(cache_capacity), n_q_heads, n_kv_heads, head_dim,
-                        b * n_q_heads, dws).total;
+                        b * n_q_heads, dws, 2).total;
 }
 
 int bifocal_decode_step(const void* q_raw, const void* k_raw, const void* v_new, void* k_cache, void* v_cache,
@@ -424,7 +429,7 @@ int bifocal_decode_unfused(const void* q, const void* k_cache, const void* v_cac
   const size_t b = static_cast<size_t>(batch);
   const size_t dws_bytes = bifocal_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, cache_capacity);
   const UnfusedLayout u = unfused_layout(b, b * static_cast<size_t>(cache_capacity), n_q_heads, n_kv_heads,
-                                         head_dim, b * n_q_heads, dws_bytes);
+                                         head_dim, b * n_q_heads, dws_bytes, 2);
   char* ws = static_cast<char*>(workspace);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t G = bifocal_group_size(L, w_pretrained);

@@ -13,6 +13,7 @@ struct PrefillLaunch {
   void* krot;  // NULL: fused in-kernel key rotation; else workspace for K' (prerotated mode)
   const void* v;
   void* o;
+  float* o32 = nullptr;  // with local_only: O written here in fp32 (same layout) instead of to o
   float* lse;
   int batch, n_q_heads, n_kv_heads, head_dim;
   int L;       // keys 0..L-1; the query rows are positions L - Lq .. L - 1
@@ -58,7 +59,8 @@ struct RotateRowsLaunch {
 };
 
 // Inclusion-exclusion merge of three attention passes: O_X [batch, rows, n_q_heads, head_dim]
-// bf16, LSE_X [batch, n_q_heads, rows] fp32; has_window == false: passes A and C are empty.
+// (bf16, or fp32 with f32_in), LSE_X [batch, n_q_heads, rows] fp32; has_window == false: passes
+// A and C are empty.
 struct Merge3Launch {
   const void* oa;
   const void* ob;
@@ -70,6 +72,7 @@ struct Merge3Launch {
   float* lse;
   int batch, rows, n_q_heads, head_dim;
   bool has_window;
+  bool f32_in = false;
 };
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);

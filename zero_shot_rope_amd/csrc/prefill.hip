@@ -55,6 +55,7 @@ struct PrefillArgs {
   const uint16_t* krot;  // prerotated mode: K' = R(Delta) K~, same layout as k
   const uint16_t* v;
   uint16_t* o;
+  float* o32;  // local-only launches: when set, O is written here in fp32 instead of bf16 to o
   float* lse;
   int B, Hq, Hkv;
   int L;       // keys 0..L-1 (the total length); query rows are the last Lq positions
@@ -503,16 +504,32 @@ void prefill_kernel(const PrefillArgs<D> a) {
   const float den = w_a + w_r;
   const float inv = 1.0f / den;
   if (qi < L) {
-    uint16_t* dst = a.o + ((size_t)b * a.Lq + (qi - a.q0)) * q_row_stride + (size_t)head * D;
+    const size_t orow = ((size_t)b * a.Lq + (qi - a.q0)) * q_row_stride + (size_t)head * D;
+    bool done = false;
+    if constexpr (MODE == kLocalOnly) {
+      if (a.o32 != nullptr) {
+        float* dst = a.o32 + orow;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 out;
-        out[0] = pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-        out[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * g + 4 * h) = out;
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * g + 4 * h) =
+                f32x4{o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+        done = true;
       }
+    }
+    if (!done) {
+      uint16_t* dst = a.o + orow;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 out;
+          out[0] = pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+          out[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * g + 4 * h) = out;
+        }
+    }
     if (a.lse != nullptr && h == 0)
       a.lse[((size_t)b * a.Hq + head) * a.Lq + (qi - a.q0)] = (m_run + __log2f(den)) * 0.69314718055994531f;
   }
@@ -553,6 +570,7 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
   a.krot = static_cast<const uint16_t*>(p.krot);
   a.v = static_cast<const uint16_t*>(p.v);
   a.o = static_cast<uint16_t*>(p.o);
+  a.o32 = p.o32;
   a.lse = p.lse;
   a.B = p.batch;
   a.Hq = p.n_q_heads;

@@ -46,13 +46,31 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const uint16_t* __rest
   *reinterpret_cast<u32x4*>(dst + d + HALF) = hi;
 }
 
-// Inclusion-exclusion merge of the three passes. O_X [B, Lr, Hq, D] bf16, LSE_X [B, Hq, Lr] fp32
-// (natural log). With has_window == 0 (w0 = 0) passes A and C have no pairs and are not read.
+// Inclusion-exclusion merge of the three passes. O_X [B, Lr, Hq, D] (T: uint16_t for bf16, float
+// for fp32), LSE_X [B, Hq, Lr] fp32 (natural log). With has_window == 0 (w0 = 0) passes A and C have no pairs and are not read.
 // One thread per 8 output elements; the weights are relative to M = max(LSE_A, LSE_B), which
 // bounds all three (C's pairs are a subset of B's).
-template <int D>
-__global__ __launch_bounds__(256) void merge3_kernel(const uint16_t* __restrict__ oa, const uint16_t* __restrict__ ob,
-                                                     const uint16_t* __restrict__ oc, const float* __restrict__ la,
+// Eight consecutive pass-output values as floats.
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16lo(w[e]);
+    x[2 * e + 1] = bf16hi(w[e]);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(256) void merge3_kernel(const T* __restrict__ oa, const T* __restrict__ ob,
+                                                     const T* __restrict__ oc, const float* __restrict__ la,
                                                      const float* __restrict__ lb, const float* __restrict__ lc,
                                                      uint16_t* __restrict__ o, float* __restrict__ lse,
                                                      long long n_units, int Lr, int Hq, int has_window) {
@@ -76,17 +94,17 @@ __global__ __launch_bounds__(256) void merge3_kernel(const uint16_t* __restrict_
   const float wc = has_window ? __expf(lse_c - M) : 0.f;
   const float den = wa + wb - wc;
   const float inv = 1.0f / den;
-  const u32x4 xb = *reinterpret_cast<const u32x4*>(ob + oi);
-  u32x4 xa = u32x4{0, 0, 0, 0}, xc = u32x4{0, 0, 0, 0};
+  float xa[8] = {}, xb[8], xc[8] = {};
+  load8(ob + oi, xb);
   if (has_window) {
-    xa = *reinterpret_cast<const u32x4*>(oa + oi);
-    xc = *reinterpret_cast<const u32x4*>(oc + oi);
+    load8(oa + oi, xa);
+    load8(oc + oi, xc);
   }
   u32x4 out;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const float y0 = (wa * bf16lo(xa[w]) + wb * bf16lo(xb[w]) - wc * bf16lo(xc[w])) * inv;
-    const float y1 = (wa * bf16hi(xa[w]) + wb * bf16hi(xb[w]) - wc * bf16hi(xc[w])) * inv;
+    const float y0 = (wa * xa[2 * w] + wb * xb[2 * w] - wc * xc[2 * w]) * inv;
+    const float y1 = (wa * xa[2 * w + 1] + wb * xb[2 * w + 1] - wc * xc[2 * w + 1]) * inv;
     out[w] = pack_bf16x2(y0, y1);
   }
   *reinterpret_cast<u32x4*>(o + oi) = out;
@@ -111,22 +129,26 @@ hipError_t launch_rotate_rows(const RotateRowsLaunch& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+template <int D, typename T>
+static void merge3_d(const Merge3Launch& p, dim3 grid, long long units, hipStream_t stream) {
+  hipLaunchKernelGGL((merge3_kernel<D, T>), grid, dim3(256), 0, stream, static_cast<const T*>(p.oa),
+                     static_cast<const T*>(p.ob), static_cast<const T*>(p.oc), p.la, p.lb, p.lc,
+                     static_cast<uint16_t*>(p.o), p.lse, units, p.rows, p.n_q_heads, p.has_window ? 1 : 0);
+}
+
 hipError_t launch_merge3(const Merge3Launch& p, hipStream_t stream) {
   const long long units = (long long)p.batch * p.rows * p.n_q_heads * (p.head_dim / 8);
   if (units <= 0 || (units + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((units + 255) / 256));
-  const auto* oa = static_cast<const uint16_t*>(p.oa);
-  const auto* ob = static_cast<const uint16_t*>(p.ob);
-  const auto* oc = static_cast<const uint16_t*>(p.oc);
-  auto* o = static_cast<uint16_t*>(p.o);
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(merge3_kernel<128>, grid, dim3(256), 0, stream, oa, ob, oc, p.la, p.lb, p.lc, o, p.lse, units,
-                       p.rows, p.n_q_heads, p.has_window ? 1 : 0);
-  else if (p.head_dim == 64)
-    hipLaunchKernelGGL(merge3_kernel<64>, grid, dim3(256), 0, stream, oa, ob, oc, p.la, p.lb, p.lc, o, p.lse, units,
-                       p.rows, p.n_q_heads, p.has_window ? 1 : 0);
-  else
+  if (p.head_dim == 128) {
+    if (p.f32_in) merge3_d<128, float>(p, grid, units, stream);
+    else merge3_d<128, uint16_t>(p, grid, units, stream);
+  } else if (p.head_dim == 64) {
+    if (p.f32_in) merge3_d<64, float>(p, grid, units, stream);
+    else merge3_d<64, uint16_t>(p, grid, units, stream);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
