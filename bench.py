@@ -73,7 +73,7 @@ MEASURED_TRAFFIC = {
     # rotate_keys_kernel + prefill_kernel<128, prerotated> at the 128K Qwen3-8B shape.
     "prefill": {"sources": "70e397111455e9ca", "fetch_bytes": 20092.55e6, "write_bytes": 1542.49e6},
     # decode_split_kernel + decode_reduce_kernel, mean over the 512 steps (L 98001..98512).
-    "decode": {"sources": "77822ba9bae08d86", "fetch_bytes": 407.07e6, "write_bytes": 4.33e6},
+    "decode": {"sources": "f10c98a5d45fbe6d", "fetch_bytes": 407.06e6, "write_bytes": 4.33e6},
 }
 # The files holding the measured kernels' device code and launch geometry.
 _KERNEL_SOURCES = {
@@ -314,6 +314,33 @@ def main():
             "us_per_call": round(vms * 1e3, 2), "GB/s": round(vbytes / (vms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(vbytes / (vms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "bytes_per_call": vbytes}
         del vk, vv, vq, vo, vws
+
+        # A serving batch: 1024 sequences of 256 to 2048 keys (seeded uniform lengths), Qwen3-8B
+        # heads, one call. Its 4.8 GB of cache per call is 19x the last-level cache, so no call
+        # finds the previous one's data there.
+        sB, scap = 1024, 2048
+        slens = np.random.default_rng(9).integers(256, scap + 1, size=sB).astype(np.int32)
+        gen = torch.Generator(device=dev).manual_seed(9)
+        sk = torch.randn((sB, scap, dcfg.n_kv_heads, dcfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        sv = torch.randn((sB, scap, dcfg.n_kv_heads, dcfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        sq = torch.randn((sB, dcfg.n_q_heads, dcfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        so = torch.empty_like(sq)
+        slen_t = torch.from_numpy(slens).to(dev)
+        sws_b = Z.bifocal_decode_varlen_workspace_bytes(sB, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim, scap)
+        sws = torch.empty(sws_b, dtype=torch.uint8, device=dev)
+
+        def scall():
+            Z.bifocal_decode_varlen(sq, sk, sv, so, None, sB, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
+                                    slen_t, scap, scap, dcfg.w0, dcfg.w_pretrained, dcfg.rope_theta, sws, sws_b, sptr)
+        scall()
+        sms = float(np.median(event_times(torch, stream, scall, 10)))
+        sbytes = 4096.0 * float(slens.sum())
+        decode["batched_varlen_serving"] = {
+            "what": f"one call, {sB} sequences of 256..{scap} keys (seeded uniform lengths), Qwen3-8B heads",
+            "us_per_call": round(sms * 1e3, 2), "GB/s": round(sbytes / (sms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(sbytes / (sms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "bytes_per_call": sbytes,
+            "workspace_bytes": sws_b}
+        del sk, sv, sq, so, sws
 
         # The same 512 steps taking in each new token raw: base RoPE of its query and key at p = L - 1,
         # key and value written into cache row p, then the decode (two launches per step).

@@ -180,7 +180,9 @@ int bifocal_decode_step(const void* q_raw, const void* k_raw, const void* v_new,
                         int64_t L, int64_t cache_capacity, int64_t w0, int64_t w_pretrained,
                         double rope_theta, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace bifocal_decode_varlen needs for lengths <= max_len with these shapes.
+/* Bytes of device workspace bifocal_decode_varlen needs with these shapes, at any lengths:
+ * (workgroups + batch) partial records of n_q_heads x (head_dim + 2) floats, workgroups = 256 per
+ * group of 8 KV heads (rounded up), then two int32 per sequence. Linear in the batch.
  * Returns 0 for invalid arguments. */
 size_t bifocal_decode_varlen_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                              int64_t max_len);
@@ -190,15 +192,15 @@ size_t bifocal_decode_varlen_workspace_bytes(int batch, int n_q_heads, int n_kv_
  * G_b = max(1, ceil(L_b / w_pretrained)) (review page, Method: G follows the current length).
  *   seq_lens  [batch] int32 DEVICE array of the lengths L_b; values outside [1, max_len] are
  *             clamped into it
- *   max_len   host-side upper bound of every L_b: sizes the split grid and the workspace;
- *             1 <= max_len <= cache_capacity
+ *   max_len   host-side upper bound of every L_b; 1 <= max_len <= cache_capacity
  *   q, k_cache, v_cache, o, lse, w0, w_pretrained, rope_theta, stream: as bifocal_decode;
  *   workspace >= bifocal_decode_varlen_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
  *             max_len).
- * The device cuts the whole batch's keys into chunks of one length, chosen from the lengths so
- * that every chunk fits one grid of about one workgroup per CU, whatever the mix of lengths.
- * Sequence b's output is bifocal_decode of that sequence alone at L = L_b, up to the rounding
- * of a different chunking (the partials merge in another order).
+ * The device lays the 32-key blocks of all sequences end to end and gives each workgroup of one
+ * grid (about one per CU) an equal run of them, whatever the mix of lengths; a run may hold the
+ * end of one sequence and the start of the next. Sequence b's output is bifocal_decode of that
+ * sequence alone at L = L_b, up to the rounding of a different split (the partials merge in
+ * another order).
  * Returns BIFOCAL_OK or a negative bifocal_status (BIFOCAL_EINVAL when seq_lens is NULL). */
 int bifocal_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                           int batch, int n_q_heads, int n_kv_heads, int head_dim,

@@ -183,12 +183,14 @@ def test_decode_varlen_rejects_before_any_hip_call(lib, kw, expect):
 
 def test_decode_varlen_workspace_query(lib):
     assert lib.bifocal_decode_varlen_workspace_bytes(0, 8, 2, 128, 100) == 0
-    prev = 0
-    for L in [1, 33, 4096, 98001, 131072]:
-        n = lib.bifocal_decode_varlen_workspace_bytes(3, 32, 8, 128, L)
-        assert n >= prev and n % (3 * 32 * 130 * 4) == 0
-        assert n >= lib.bifocal_decode_workspace_bytes(3, 32, 8, 128, L)
-        prev = n
+    # One partial record (all query heads, D + 2 floats each) per segment: at most one grid of
+    # workgroups (256 per KV-head group of 8) plus the batch; then a (first, count) int32 pair per
+    # sequence. Linear in the batch and independent of the length.
+    for B, Hq, Hkv, D in [(3, 32, 8, 128), (4096, 32, 8, 128), (5, 64, 16, 64)]:
+        wgs = -(-256 // -(-Hkv // 8))
+        want = (wgs + B) * Hq * (D + 2) * 4 + B * 8
+        for L in [1, 33, 98001, 131072]:
+            assert lib.bifocal_decode_varlen_workspace_bytes(B, Hq, Hkv, D, L) == want
     need = lib.bifocal_decode_varlen_workspace_bytes(3, 8, 2, 128, 100)
     assert varlen_call(lib, wsb=need - 1) == EWS
 

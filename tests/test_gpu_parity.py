@@ -611,6 +611,12 @@ SMALL_VARLEN = [
     (4000, 8, 2, 128, 512, 64, 1e6, [4000] + [1] * 5 + [33] * 5),               # one long, many tiny
     (900, 16, 2, 128, 256, 64, 1e6, [900, 450, 3]),                              # GQA 8:1
     (60, 4, 1, 64, 32, 8, 1e4, [1 + (13 * i) % 60 for i in range(300)]),         # 300 sequences, 5 scan rounds
+    # 400 sequences up to 2000 keys: workgroup runs of 50 blocks split some sequences and join others
+    (2000, 4, 1, 64, 512, 32, 1e4, [1 + (97 * i * i + 31 * i) % 2000 for i in range(400)]),
+    # 1000 short sequences: every run crosses several sequences
+    (200, 4, 1, 64, 64, 8, 1e4, [1 + (7 * i) % 200 for i in range(1000)]),
+    # 16 KV heads: two head groups, 128 workgroups each
+    (640, 32, 16, 64, 128, 40, 1e6, [640 - 31 * i for i in range(20)]),
 ]
 
 

@@ -197,10 +197,12 @@ size_t bifocal_decode_varlen_workspace_bytes(int batch, int n_q_heads, int n_kv_
                                              int64_t max_len) {
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1 || max_len < 1) return 0;
   if (max_len > kMaxL || n_q_heads % n_kv_heads != 0) return 0;
-  // One slot per workgroup of the batch-wide chunking, for every sequence (a sequence can own at
-  // most all of them); independent of the lengths, which only the device knows.
-  const long long slots = bifocal::decode_varlen_slots(batch, n_kv_heads);
-  return static_cast<size_t>(batch) * n_q_heads * slots * (head_dim + 2) * sizeof(float);
+  // One partial record (all query heads) per segment: a workgroup's run and a sequence meet in at
+  // most workgroups + batch segments. Then a (first workgroup, count) pair per sequence.
+  // Independent of the lengths, which only the device knows.
+  const long long records = bifocal::decode_varlen_slots(batch, n_kv_heads) + batch;
+  return static_cast<size_t>(records) * n_q_heads * (head_dim + 2) * sizeof(float) +
+         static_cast<size_t>(batch) * 2 * sizeof(int32_t);
 }
 
 // Shared by the single-length and the per-sequence-length decode. lens == NULL: every sequence has
@@ -222,7 +224,7 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   // The query heads of one KV head are the 16 columns of the decode kernel's MFMA tile.
   if (n_q_heads / n_kv_heads > 16) return BIFOCAL_EUNSUPPORTED;
   if (cache_capacity > kMaxL || batch > 65535) return BIFOCAL_EUNSUPPORTED;  // grid z limit
-  if (lens != nullptr && (long double)batch * n_q_heads * bifocal::decode_varlen_slots(batch, n_kv_heads) *
+  if (lens != nullptr && ((long double)bifocal::decode_varlen_slots(batch, n_kv_heads) + batch) * n_q_heads *
                                (head_dim + 2) * 4 >= 4.0e18L)
     return BIFOCAL_EUNSUPPORTED;  // workspace size beyond size_t arithmetic
   const size_t need = lens ? bifocal_decode_varlen_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, L)
@@ -234,8 +236,8 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
   uint32_t W[64];
   phase_increments(head_dim, rope_theta, W);
   // One length: the batch shares one grid of about one workgroup per CU. Per-sequence lengths:
-  // the device cuts the whole batch's keys into chunks of one length, over a grid of
-  // decode_varlen_slots workgroups.
+  // the device lays the 32-key blocks of all sequences end to end and gives each of the
+  // decode_varlen_slots workgroups an equal run of them.
   const bifocal::DecodeSplit s = bifocal::decode_split(L, batch, n_kv_heads);
   bifocal::DecodeLaunch p;
   p.q = q;

@@ -11,12 +11,14 @@
 //   double-buffered swizzled tile read back transposed for O^T = V^T P^T. Local and remote
 //   contributions share one running max; the wave writes the partial (max, sum, unnormalised
 //   output) of its chunk to the workspace.
-// Per-sequence lengths: one chunk length for the whole batch, chosen on the device from the
-//   lengths so that every chunk of every sequence fits one grid of about one workgroup per CU.
+// Per-sequence lengths: the 32-key blocks of all sequences are laid end to end and every
+//   workgroup of one grid (about one per CU) takes an equal run of them, which may cross
+//   sequence boundaries: it walks its run one segment (the part of one sequence) at a time and
+//   writes one partial per segment. The reduce merges each sequence's segments.
 // Decode step on a raw new token: every workgroup applies base RoPE at p = L - 1 to its raw
 //   query columns in registers; the workgroup whose chunk ends at L also takes the raw key and
 //   value of position p, uses them for row p, and writes them into cache row p.
-// Reduce kernel: merges the partials of all chunks by log-sum-exp and writes bf16 o / lse.
+// Reduce kernels: merge the partials of all chunks (segments) by log-sum-exp and write bf16 o / lse.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -83,53 +85,73 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Per-sequence lengths: the batch's keys are cut into chunks of one length, chosen from the
-// device-side lengths so that sum_b ceil(L_b / chunk) <= slots (the grid's x size, target + B):
-// chunk = max(32, total / (slots - B) rounded up to a multiple of 32), since
-// sum_b ceil(L_b / chunk) <= total / chunk + B. Every workgroup then carries about the same
-// number of keys, whatever the mix of lengths. Lengths are clamped to [1, maxL].
+// Per-sequence lengths, flattened: sequence i contributes ceil(L_i / 32) blocks (lengths clamped
+// to [1, maxL]), the blocks of all sequences are numbered end to end (sequence order, then block
+// order), and workgroup w of nwg takes blocks [w * nb, (w + 1) * nb) with nb = ceil(total / nwg).
+// Its run covers one or more segments (the part of one sequence inside the run); the segment of
+// sequence i in workgroup w writes partial record w + i, distinct for every segment and below
+// nwg + B. Every workgroup carries at most nb blocks whatever the mix of lengths.
 __device__ __forceinline__ int varlen_len(const int32_t* lens, int i, int maxL) { return min(max(lens[i], 1), maxL); }
-
-// Run by one wave: the chunk length (and, with want >= 0, the sequence and split of workgroup
-// `want`; b_out = -1 when it has no chunk). Lanes take 64 sequences at a time.
-__device__ __forceinline__ int varlen_plan(const int32_t* lens, int B, int maxL, int slots, int want, int& b_out,
-                                           int& split_out) {
-  const int lane = threadIdx.x & 63;
-  long long tot = 0;
-  for (int i0 = 0; i0 < B; i0 += 64) tot += (i0 + lane < B) ? varlen_len(lens, i0 + lane, maxL) : 0;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
-  const long long per = (tot + (slots - B) - 1) / (slots - B);
-  // Never longer than the longest sequence needs (one chunk each then, B <= slots).
-  const long long cap = ((long long)maxL + 31) / 32 * 32;
-  const int chunk = (int)min(cap, max(32LL, (per + 31) / 32 * 32));
-  b_out = -1;
-  split_out = 0;
-  if (want < 0) return chunk;
-  int base = 0;  // first split index of the current 64 sequences
-  for (int i0 = 0; i0 < B && b_out < 0; i0 += 64) {
-    const int i = i0 + lane;
-    const int n = (i < B) ? (varlen_len(lens, i, maxL) + chunk - 1) / chunk : 0;
-    int incl = n;  // inclusive prefix over the wave
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int up = __shfl_up(incl, off);
-      if (lane >= off) incl += up;
-    }
-    const int excl = base + incl - n;
-    const bool mine = (i < B) && want >= excl && want < excl + n;
-    const unsigned long long hit = __builtin_amdgcn_ballot_w64(mine);
-    if (hit) {
-      const int src = __builtin_ctzll(hit);
-      b_out = i0 + src;
-      split_out = want - __shfl(excl, src);
-    }
-    base += __shfl(incl, 63);
-  }
-  return chunk;
+__device__ __forceinline__ int varlen_blocks(const int32_t* lens, int i, int maxL) {
+  return (varlen_len(lens, i, maxL) + 31) / 32;
 }
 
-template <int D>
+// Run by one wave: workgroup w's run. b0 = its first sequence, start = its first block within b0,
+// remaining = blocks in the run (0: no work), P0 = blocks of the sequences before b0, nb = run
+// length. Lane l first sums the blocks of sequences [l m, (l + 1) m), m = ceil(B / 64) (loads
+// independent of each other); a scan over the lanes finds the lane holding block w * nb, whose m
+// sequences are then scanned 64 at a time.
+__device__ __forceinline__ void varlen_flat_plan(const int32_t* lens, int B, int maxL, int nwg, int w, int& b0,
+                                                 int& start, int& remaining, long long& P0, long long& nb) {
+  const int lane = threadIdx.x & 63;
+  const int m = (B + 63) / 64;
+  const int lo = min(lane * m, B), hi = min(lo + m, B);
+  long long sum = 0;
+  for (int i = lo; i < hi; ++i) sum += varlen_blocks(lens, i, maxL);
+  long long incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
+  }
+  const long long total = __shfl(incl, 63);
+  nb = (total + nwg - 1) / nwg;
+  const long long first = (long long)w * nb;
+  b0 = -1;
+  start = 0;
+  remaining = 0;
+  P0 = 0;
+  if (first >= total) return;
+  remaining = (int)min(nb, total - first);
+  const long long excl = incl - sum;
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(first >= excl && first < incl);
+  const int src = __builtin_ctzll(hit);
+  const int lo_s = __shfl(lo, src), hi_s = __shfl(hi, src);
+  long long base = __shfl(excl, src);
+  for (int j0 = lo_s; j0 < hi_s && b0 < 0; j0 += 64) {
+    const int j = j0 + lane;
+    const int n = (j < hi_s) ? varlen_blocks(lens, j, maxL) : 0;
+    long long inc = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long up = __shfl_up(inc, off);
+      if (lane >= off) inc += up;
+    }
+    const long long ex = base + inc - n;
+    const unsigned long long h2 = __builtin_amdgcn_ballot_w64(j < hi_s && first >= ex && first < ex + n);
+    if (h2) {
+      const int sj = __builtin_ctzll(h2);
+      b0 = j0 + sj;
+      P0 = __shfl(ex, sj);
+      start = (int)(first - P0);
+    }
+    base += __shfl(inc, 63);
+  }
+}
+
+// VAR: per-sequence lengths (flattened runs, lens != NULL); else one length, grid (split,
+// KV-head group, batch).
+template <int D, bool VAR>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_split_kernel(const DecodeArgs<D> a) {
   constexpr int HALF = D / 2;
@@ -147,42 +169,15 @@ void decode_split_kernel(const DecodeArgs<D> a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;  // MFMA 16x16 lane = li + 16 * lg
-  // One length: grid (split, KV-head group, batch). Per-sequence lengths: grid (slot, KV-head
-  // group); wave 0 maps the slot to a (sequence, split) of the batch-wide chunking, and slots past
-  // the last chunk exit.
-  int split = (int)blockIdx.x, b = (int)blockIdx.z, chunk = a.chunk;
-  if (a.lens != nullptr) {
-    // The plan travels through the second angle table, which is first written after the first
-    // block's barrier, long after every wave has read it here.
-    int* s_plan = reinterpret_cast<int*>(s_t1);
-    if (wave == 0) {
-      int pb, ps;
-      const int c = varlen_plan(a.lens, a.B, a.L, a.n_splits, (int)blockIdx.x, pb, ps);
-      if (lane == 0) {
-        s_plan[0] = pb;
-        s_plan[1] = ps;
-        s_plan[2] = c;
-      }
-    }
-    __syncthreads();
-    b = s_plan[0];
-    split = s_plan[1];
-    chunk = s_plan[2];
-    if (b < 0) return;
-  }
+  // One segment: keys [k_begin, k_end) of sequence b (length L, group size G, window w0, both as
+  // the host sets them for a single length); the partial of query head h goes to
+  // rec + h * head_stride.
+  auto segment = [&](int b, int L, int G, int w0, int k_begin, int k_end, float* rec, size_t head_stride)
+                     __attribute__((always_inline)) {
   const int g = blockIdx.y * kDecWaves + wave;  // KV head of this wave
   const bool head_live = g < a.Hkv;
   const int gl = head_live ? g : 0;
   const int Hg = a.Hq / a.Hkv;
-  // This sequence's length, group size and window: the launch's, or from its own length (lengths
-  // clamped to [1, maximum length]; G = max(1, ceil(L / w_pretrained)); w0 := L when G = 1 or
-  // w0 >= L, as the host does for a single length).
-  int L = a.L, G = a.G, w0 = a.w0;
-  if (a.lens != nullptr) {
-    L = min(max(a.lens[b], 1), a.L);
-    G = (L - 1) / a.wp + 1;
-    if (G == 1 || w0 >= L) w0 = L;
-  }
   const int p = L - 1;
   const int dq = correction_offset(p, G);
 
@@ -210,8 +205,6 @@ void decode_split_kernel(const DecodeArgs<D> a) {
   const size_t row_stride = (size_t)a.Hkv * D;
   const uint16_t* kbase = a.kc + (size_t)b * a.cap * row_stride + (size_t)gl * D;
   const uint16_t* vbase = a.vc + (size_t)b * a.cap * row_stride + (size_t)gl * D;
-  const int k_begin = split * chunk;
-  const int k_end = min(L, k_begin + chunk);
   const int nblk = (k_end - k_begin + kDecBlock - 1) / kDecBlock;
   // LDS buffers are named statically (buffer 0/1 of V and of the angle table) and indexed with
   // one integer offset, so the compiler can tell every LDS read from the direct loads in flight
@@ -402,7 +395,7 @@ void decode_split_kernel(const DecodeArgs<D> a) {
       w[e] = lg < 2 ? (lg == 0 ? w0 : w1) : (lg == 2 ? w2 : w3);
     }
   };
-  if (a.k_new != nullptr) {
+  if (!VAR && a.k_new != nullptr) {
     // Raw query: base RoPE at p (the same fixed-point phase as the correction angles).
 #pragma unroll
     for (int c = 0; c < NQC / 2; ++c) {
@@ -431,7 +424,7 @@ void decode_split_kernel(const DecodeArgs<D> a) {
       // by base RoPE at p) replaces the K registers of row p and the value the V tile's row p,
       // and both go to cache row p. Rows past p, which the loads clamp to row p, take the same
       // key and value, so the masked keys see exactly the data of a cache that already held them.
-      const bool new_tok = a.k_new != nullptr && k_end == L;
+      const bool new_tok = !VAR && a.k_new != nullptr && k_end == L;
       const size_t new_row = ((size_t)b * a.Hkv + gl) * D;
       u32x4 kn_raw[NQC], vn_raw;
       if (new_tok) {
@@ -494,7 +487,7 @@ void decode_split_kernel(const DecodeArgs<D> a) {
   l_tot = pair_sum(l_tot);
   if (q_live) {
     const int head = g * Hg + li;
-    float* dst = a.ws + (((size_t)b * a.Hq + head) * a.n_splits + split) * (D + 2);
+    float* dst = rec + (size_t)head * head_stride;
     if (lg == 0) {
       dst[0] = m_run;
       dst[1] = l_tot;
@@ -504,6 +497,62 @@ void decode_split_kernel(const DecodeArgs<D> a) {
     for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[2 + 16 * ob + 4 * lg + r] = o[ob][r];
+  }
+  };  // segment
+
+  if constexpr (!VAR) {
+    const int b = (int)blockIdx.z, split = (int)blockIdx.x;
+    const int k_begin = split * a.chunk;
+    segment(b, a.L, a.G, a.w0, k_begin, min(a.L, k_begin + a.chunk),
+            a.ws + ((size_t)b * a.Hq * a.n_splits + split) * (D + 2), (size_t)a.n_splits * (D + 2));
+  } else {
+    // Wave 0 plans this workgroup's run; the plan travels through the second angle table, which a
+    // segment first writes after its first barrier, when every wave has read the plan.
+    int* s_plan = reinterpret_cast<int*>(s_t1);
+    if (wave == 0) {
+      int b0, start, rem;
+      long long P0, nb;
+      varlen_flat_plan(a.lens, a.B, a.L, (int)gridDim.x, (int)blockIdx.x, b0, start, rem, P0, nb);
+      if (lane == 0) {
+        s_plan[0] = b0;
+        s_plan[1] = start;
+        s_plan[2] = rem;
+        s_plan[3] = (int)(P0 & 0xffffffffLL);
+        s_plan[4] = (int)(P0 >> 32);
+        s_plan[5] = (int)(nb & 0xffffffffLL);
+        s_plan[6] = (int)(nb >> 32);
+      }
+    }
+    __syncthreads();
+    const int w = (int)blockIdx.x;
+    int b = __builtin_amdgcn_readfirstlane(s_plan[0]);
+    int start = __builtin_amdgcn_readfirstlane(s_plan[1]);
+    int rem = __builtin_amdgcn_readfirstlane(s_plan[2]);
+    long long P = (long long)(uint32_t)__builtin_amdgcn_readfirstlane(s_plan[3]) |
+                  ((long long)__builtin_amdgcn_readfirstlane(s_plan[4]) << 32);
+    const long long nb = (long long)(uint32_t)__builtin_amdgcn_readfirstlane(s_plan[5]) |
+                         ((long long)__builtin_amdgcn_readfirstlane(s_plan[6]) << 32);
+    // Per sequence, after the nwg + B partial records: (first workgroup, number of workgroups),
+    // written by the workgroup that holds the sequence's first block.
+    int* info = reinterpret_cast<int*>(a.ws + (size_t)(gridDim.x + a.B) * a.Hq * (D + 2));
+    while (rem > 0) {
+      const int Lb = varlen_len(a.lens, b, a.L);
+      const int nbk = (Lb + kDecBlock - 1) / kDecBlock;
+      const int take = min(nbk - start, rem);
+      if (start == 0 && blockIdx.y == 0 && tid == 0) {
+        info[2 * b] = w;
+        info[2 * b + 1] = (int)((P + nbk - 1) / nb - w + 1);
+      }
+      // G = max(1, ceil(L / w_pretrained)); w0 := L when G = 1 or w0 >= L, as for one length.
+      const int Gb = (Lb - 1) / a.wp + 1;
+      const int w0b = (Gb == 1 || a.w0 >= Lb) ? Lb : a.w0;
+      segment(b, Lb, Gb, w0b, kDecBlock * start, min(Lb, kDecBlock * (start + take)),
+              a.ws + (size_t)(w + b) * a.Hq * (D + 2), (size_t)(D + 2));
+      rem -= take;
+      P += nbk;
+      ++b;
+      start = 0;
+    }
   }
 }
 
@@ -520,43 +569,35 @@ constexpr int kRedBatch = 16;  // splits per thread per load round
 
 template <int D>
 __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
-                                                                    float* __restrict__ lse, int Hq, int n_splits,
-                                                                    const int32_t* __restrict__ lens, int B, int maxL) {
+                                                                    float* __restrict__ lse, int Hq, int n_splits) {
   __shared__ float s_m[kRedGroups], s_l[kRedGroups];
   __shared__ float s_acc[kRedGroups][kRedDims];
   const int head = blockIdx.x, slice = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
   const int c = t % kRedDims, grp = t / kRedDims;
-  // n_splits is the slot stride; with per-sequence lengths this sequence has ceil(L_b / chunk).
-  int n_have = n_splits;
-  if (lens != nullptr) {
-    __shared__ int s_n;
-    if (wave == 0) {
-      int pb, ps;
-      const int chunk = varlen_plan(lens, B, maxL, n_splits, -1, pb, ps);
-      if (lane == 0) s_n = (varlen_len(lens, b, maxL) + chunk - 1) / chunk;
-    }
-    __syncthreads();
-    n_have = s_n;
-  }
+  // n_splits partials per (sequence, head), consecutive.
+  const int n_have = n_splits;
   const float* src = ws + ((size_t)b * Hq + head) * n_splits * (D + 2);
+  constexpr size_t sstride = D + 2;
   // Running (max, sum, output) of this thread's splits; absent splits weigh exp2(kNegBig - max).
   float m = kNegBig, l = 0.f, acc = 0.f;
   for (int s0 = grp; s0 < n_have; s0 += kRedGroups * kRedBatch) {
-    float ms[kRedBatch], ls[kRedBatch], os[kRedBatch];
+    // All loads of the batch first, then the masking of absent splits, so the batch is one
+    // round trip (the compiler otherwise may wait on each load to reuse its register).
+    f32x2 mls[kRedBatch];
+    float os[kRedBatch];
 #pragma unroll
     for (int u = 0; u < kRedBatch; ++u) {
-      const int sp = s0 + kRedGroups * u;
-      const float* ps = src + (size_t)min(sp, n_have - 1) * (D + 2);
-      const f32x2 ml = *reinterpret_cast<const f32x2*>(ps);  // rows are 8-byte aligned: D + 2 is even
-      ms[u] = ml[0];
-      ls[u] = ml[1];
+      const float* ps = src + (size_t)min(s0 + kRedGroups * u, n_have - 1) * sstride;
+      mls[u] = *reinterpret_cast<const f32x2*>(ps);  // rows are 8-byte aligned: D + 2 is even
       os[u] = ps[2 + kRedDims * slice + c];
-      if (sp >= n_have) {
-        ms[u] = kNegBig;
-        ls[u] = 0.f;
-        os[u] = 0.f;
-      }
+    }
+    float ms[kRedBatch], ls[kRedBatch];
+#pragma unroll
+    for (int u = 0; u < kRedBatch; ++u) {
+      const bool live = s0 + kRedGroups * u < n_have;
+      ms[u] = live ? mls[u][0] : kNegBig;
+      ls[u] = live ? mls[u][1] : 0.f;
+      os[u] = live ? os[u] : 0.f;
     }
     float mx = m;
 #pragma unroll
@@ -594,9 +635,95 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce_kernel(const float*
   }
 }
 
+// Per-sequence-length reduce: one workgroup of 4 waves per (query head, sequence). Sequence b's
+// segments sit in records first + b + s, s < n (each record holding every head), from the pair
+// (first, n) its first workgroup wrote. With many sequences a run holds few of them, so the split
+// parallelism is 4 (one wave each, up to kSeqBatch segments loaded at once) and every lane keeps
+// D / 64 dimensions; a long sequence's segments take a few more load rounds.
+constexpr int kSeqWaves = 4;
+constexpr int kSeqBatch = 8;
+
+template <int D>
+__global__ __launch_bounds__(64 * kSeqWaves) void decode_reduce_seq_kernel(const float* __restrict__ ws,
+                                                                           uint16_t* __restrict__ o,
+                                                                           float* __restrict__ lse, int Hq,
+                                                                           const int32_t* __restrict__ info) {
+  constexpr int DPL = D / 64;  // dimensions per lane
+  __shared__ float s_m[kSeqWaves], s_l[kSeqWaves];
+  __shared__ float s_acc[kSeqWaves][D];
+  const int head = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int first = info[2 * b], n_have = info[2 * b + 1];
+  const float* src = ws + ((size_t)(first + b) * Hq + head) * (D + 2);
+  const size_t sstride = (size_t)Hq * (D + 2);
+  float m = kNegBig, l = 0.f, acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  for (int s0 = wv; s0 < n_have; s0 += kSeqWaves * kSeqBatch) {
+    f32x2 mls[kSeqBatch];
+    float os[kSeqBatch][DPL];
+#pragma unroll
+    for (int u = 0; u < kSeqBatch; ++u) {
+      const float* ps = src + (size_t)min(s0 + kSeqWaves * u, n_have - 1) * sstride;
+      mls[u] = *reinterpret_cast<const f32x2*>(ps);  // records start at even floats: D + 2 is even
+      if constexpr (DPL == 2) {
+        const f32x2 v = *reinterpret_cast<const f32x2*>(ps + 2 + 2 * lane);
+        os[u][0] = v[0];
+        os[u][1] = v[1];
+      } else {
+        os[u][0] = ps[2 + lane];
+      }
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < kSeqBatch; ++u) {
+      if (s0 + kSeqWaves * u >= n_have) mls[u] = f32x2{kNegBig, 0.f};
+      mx = fmaxf(mx, mls[u][0]);
+    }
+    const float a = fast_exp2(m - mx);
+    l *= a;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] *= a;
+#pragma unroll
+    for (int u = 0; u < kSeqBatch; ++u) {
+      const float w = s0 + kSeqWaves * u < n_have ? fast_exp2(mls[u][0] - mx) : 0.f;
+      l = __builtin_fmaf(w, mls[u][1], l);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(w, os[u][e], acc[e]);
+    }
+    m = mx;
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) s_acc[wv][DPL * lane + e] = acc[e];
+  if (lane == 0) {
+    s_m[wv] = m;
+    s_l[wv] = l;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    float M = s_m[0];
+#pragma unroll
+    for (int g = 1; g < kSeqWaves; ++g) M = fmaxf(M, s_m[g]);
+    float den = 0.f, tot[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) tot[e] = 0.f;
+#pragma unroll
+    for (int g = 0; g < kSeqWaves; ++g) {
+      const float w = fast_exp2(s_m[g] - M);
+      den = __builtin_fmaf(w, s_l[g], den);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) tot[e] = __builtin_fmaf(w, s_acc[g][DPL * lane + e], tot[e]);
+    }
+    uint16_t* dst = o + ((size_t)b * Hq + head) * D + DPL * lane;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) dst[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(tot[e] / den));
+    if (lse != nullptr && lane == 0) lse[(size_t)b * Hq + head] = (M + __log2f(den)) * 0.69314718055994531f;
+  }
+}
+
 long long decode_varlen_slots(int batch, int n_kv_heads) {
+  (void)batch;  // one grid of about one workgroup per CU, whatever the batch
   const long long groups = (n_kv_heads + kDecWaves - 1) / kDecWaves;
-  return (256 + groups - 1) / groups + batch;
+  return (256 + groups - 1) / groups;
 }
 
 DecodeSplit decode_split(long long L, int batch, int n_kv_heads) {
@@ -638,15 +765,24 @@ static hipError_t launch_decode_d(const DecodeLaunch& p, hipStream_t stream) {
   for (int i = 0; i < D / 2; ++i) a.W[i] = p.W[i];
   a.B = p.batch;
   const unsigned groups = (p.n_kv_heads + kDecWaves - 1) / kDecWaves;
-  // Per-sequence lengths: n_splits is the number of slots (workgroups along x) of the batch-wide
-  // chunking, and the slot stride of the workspace.
-  const dim3 grid = p.lens ? dim3(p.n_splits, groups, 1) : dim3(p.n_splits, groups, p.batch);
-  hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(kDecThreads), 0, stream, a);
+  // Per-sequence lengths: n_splits is the number of workgroups along x (the flattened runs); the
+  // workspace holds n_splits + batch partial records, then the per-sequence (first, count) pairs.
+  const int32_t* info = nullptr;
+  if (p.lens) {
+    info = reinterpret_cast<const int32_t*>(p.workspace + (size_t)(p.n_splits + p.batch) * p.n_q_heads * (D + 2));
+    hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(p.n_splits, groups, 1), dim3(kDecThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(p.n_splits, groups, p.batch), dim3(kDecThreads), 0,
+                       stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, D / kRedDims, p.batch), dim3(kRedThreads), 0, stream,
-                     (const float*)p.workspace, static_cast<uint16_t*>(p.o), p.lse, p.n_q_heads, p.n_splits, p.lens,
-                     p.batch, p.L);
+  if (p.lens)
+    hipLaunchKernelGGL(decode_reduce_seq_kernel<D>, dim3(p.n_q_heads, p.batch), dim3(64 * kSeqWaves), 0, stream,
+                       (const float*)p.workspace, static_cast<uint16_t*>(p.o), p.lse, p.n_q_heads, info);
+  else
+    hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3(p.n_q_heads, D / kRedDims, p.batch), dim3(kRedThreads), 0, stream,
+                       (const float*)p.workspace, static_cast<uint16_t*>(p.o), p.lse, p.n_q_heads, p.n_splits);
   return hipGetLastError();
 }
 

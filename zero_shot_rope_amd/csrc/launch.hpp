@@ -89,7 +89,8 @@ struct DecodeSplit {
   int max_splits;  // upper bound on n_splits for every length <= L (workspace sizing)
 };
 DecodeSplit decode_split(long long L, int batch, int n_kv_heads);
-// Workgroups along x (and workspace slots per sequence) of a per-sequence-length decode.
+// Workgroups along x of a per-sequence-length decode (its workspace holds that many plus batch
+// partial records).
 long long decode_varlen_slots(int batch, int n_kv_heads);
 
 // Static device scratch of bifocal_decode_noalloc (its size is the public maximum in bifocal.h).
