@@ -71,7 +71,7 @@ def parse():
 # otherwise the kernel changed since the counters were taken and the traffic is reported as null.
 MEASURED_TRAFFIC = {
     # rotate_keys_kernel + prefill_kernel<128, prerotated> at the 128K Qwen3-8B shape.
-    "prefill": {"sources": "70e397111455e9ca", "fetch_bytes": 20092.55e6, "write_bytes": 1542.49e6},
+    "prefill": {"sources": "4bbf94846c33afff", "fetch_bytes": 20075.48e6, "write_bytes": 1542.28e6},
     # decode_split_kernel + decode_reduce_kernel, mean over the 512 steps (L 98001..98512).
     "decode": {"sources": "f10c98a5d45fbe6d", "fetch_bytes": 407.06e6, "write_bytes": 4.33e6},
 }

@@ -798,6 +798,55 @@ def test_decode_varlen_dominant_key():
 # fixed generator (small sizes, every row compared), prefill in its three modes, a chunk of
 # it, and decode at a few lengths on the same tensors.
 # ---------------------------------------------------------------------------------------
+def _varlen_sweep_case(i):
+    """A seeded batch for the per-sequence-length decode: batch size, length mix (uniform, all
+    equal, or one long sequence among short ones), KV heads 1 to 16 (one or two head groups of the
+    split kernel), head dim, window, pretrained window and theta. The cache stays under 3e7
+    elements per tensor."""
+    rng = np.random.default_rng(11000 + i)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 8, 16]))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    cap = int(rng.integers(1, 1500))
+    B = int(max(1, min(int(rng.integers(1, 700)), 3e7 // (cap * Hkv * D))))
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        lens = rng.integers(1, cap + 1, size=B)
+    elif kind == 1:
+        lens = np.full(B, cap)
+    else:
+        lens = rng.integers(1, max(2, cap // 20), size=B)
+        lens[rng.integers(0, B)] = cap
+    wp = int(rng.integers(1, 400))
+    w0 = int(rng.choice([0, 1, int(rng.integers(0, 300)), 10000]))
+    theta = float(rng.choice([1e4, 1e6]))
+    return cap, Hq, Hkv, D, wp, w0, theta, [int(x) for x in lens]
+
+
+VARLEN_SWEEP = [_varlen_sweep_case(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("i", range(len(VARLEN_SWEEP)),
+                         ids=[f"v{i}-B{len(c[7])}cap{c[0]}H{c[1]}-{c[2]}D{c[3]}" for i, c in enumerate(VARLEN_SWEEP)])
+def test_decode_varlen_random_sweep(i):
+    cap, Hq, Hkv, D, wp, w0, theta, lens = VARLEN_SWEEP[i]
+    B = len(lens)
+    say(f"varlen sweep {i}: B={B} cap={cap} Hq={Hq} Hkv={Hkv} D={D} wp={wp} w0={w0} theta={theta:g}")
+    rng = np.random.default_rng(12000 + i)
+    kb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    vb = W.round_to_bf16_bits(rng.standard_normal((B, cap, Hkv, D), dtype=np.float32))
+    qb = W.round_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    o, lse = run_decode_varlen(qb, kb, vb, lens, cap, w0, wp, theta)
+    # Every sequence when few, else the first, the last, the longest and 40 seeded others.
+    pick = range(B) if B <= 48 else sorted({0, B - 1, int(np.argmax(lens)), *rng.choice(B, 40, replace=False).tolist()})
+    for b in pick:
+        L = lens[b]
+        ref_o, ref_lse = bifocal_decode(f64(qb[b:b + 1, :]), f64(kb[b:b + 1, :L]), f64(vb[b:b + 1, :L]), L=L, w0=w0,
+                                        w_pretrained=wp, theta=theta)
+        compare(o[b:b + 1], ref_o, f"o seq {b} L={L}")
+        assert np.max(np.abs(lse[b:b + 1] - ref_lse)) <= LSE_ABS
+
+
 def _sweep_case(i):
     rng = np.random.default_rng(9000 + i)
     D = int(rng.choice([64, 128]))

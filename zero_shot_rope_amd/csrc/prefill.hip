@@ -319,7 +319,7 @@ void prefill_kernel(const PrefillArgs<D> a) {
   // tile (K rows 32*kb_k.. of ks into s_out, when DO_QK), slots 8-15 the PV MFMAs of the
   // previous half tile (P^T pb_prev, V rows 32*kb_v.. of vs, when DO_PV). Between them go the
   // softmax VALU of the current half tile (s_cur -> pb_cur, the exponentials against the stored
-  // max; they need none of these MFMAs) and the LDS operand reads two slots ahead.
+  // max; they need none of these MFMAs) and the LDS operand reads AHEAD slots ahead.
   // sched_barrier keeps the slot order, so the matrix unit and the VALU work side by side.
   // The rescale check closes the step.
   auto half_step = [&](auto do_qk, auto do_pv, const uint16_t* ks, int kb_k, const u32x4 (&qa)[NC], f32x16& s_out,
