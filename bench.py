@@ -70,8 +70,8 @@ def parse():
 # --copy-calibration in the same run. Valid only while the kernel sources hash to `sources`;
 # otherwise the kernel changed since the counters were taken and the traffic is reported as null.
 MEASURED_TRAFFIC = {
-    # rotate_keys_kernel + prefill_kernel<128, prerotated> at the 128K Qwen3-8B shape.
-    "prefill": {"sources": "4bbf94846c33afff", "fetch_bytes": 20075.48e6, "write_bytes": 1542.28e6},
+    # rotate_keys_kernel + prefill_wide_kernel<prerotated> at the 128K Qwen3-8B shape.
+    "prefill": {"sources": "eac98a544b1d958c", "fetch_bytes": 27052.56e6, "write_bytes": 1655.50e6},
     # decode_split_kernel + decode_reduce_kernel, mean over the 512 steps (L 98001..98512).
     "decode": {"sources": "f10c98a5d45fbe6d", "fetch_bytes": 407.06e6, "write_bytes": 4.33e6},
 }
@@ -489,7 +489,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic("prefill"),
                      "traffic_unit": "bytes per prefill call (rotate + attention kernels)",
-                     "kernel": "prefill_kernel<128, prerotated> (+ rotate_keys_kernel)", "flops_per_launch": flops},
+                     "kernel": "prefill_wide_kernel<prerotated> (+ rotate_keys_kernel)", "flops_per_launch": flops},
         "prefill_mode": "keys rotated once into a workspace, then the fused attention kernel",
         **legs,
         "decode": decode,

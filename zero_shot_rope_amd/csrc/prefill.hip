@@ -535,6 +535,398 @@ void prefill_kernel(const PrefillArgs<D> a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Wide-wave prefill (D = 128, four query heads per workgroup): a wave owns 48 query rows of one
+// head, as three 16-column blocks of v_mfma_f32_16x16x32_bf16, so every K and V operand read from
+// LDS feeds three MFMAs: 2/3 of the LDS bytes per unit of matrix work of the 32-row wave above.
+// Measured at the 128K layer shape, the narrow kernel keeps the MFMA pipe 63% busy at a clock the
+// power budget holds near 1.76 GHz; this one 50% busy at 2.26 GHz, and finishes 2-3% sooner.
+// 8 waves = 4 heads x 2 row groups: BM = 96 query rows per workgroup. Registers do not allow the
+// three-stage half step of the narrow kernel; a half step here is two phases:
+//   1. softmax of this half's scores (P, exponentials against the stored max, row sums, max fold,
+//      rescale check; a raised max scales O and the weight sum first);
+//   2. this half's PV MFMAs, then the next half's score MFMAs.
+// With no lag between scores and PV, the keys of tile t+1 are read (its first score half) before
+// the barrier of tile t+1, so K and V are triple-buffered: one barrier per tile still covers the
+// direct loads, each issued a tile before the barrier that publishes it.
+// 16x16x32 lane layout (A[i][k]: lane i + 16(k/8), element k%8; B[k][j]: lane j + 16(k/8); C[i][j]:
+// lane j + 16(i/4), register i%4): lane (li, lg) scores keys 4lg + r of each 16-key block for query
+// column li, and the PV's k order is the same permutation (element e: key 4lg + e of block 0 for
+// e < 4, of block 1 for e >= 4), so P goes to the PV MFMA from the lane's own scores.
+// ---------------------------------------------------------------------------------------------
+constexpr int kWideCols = 48;  // query rows per wave
+constexpr int kWideBM = 96;    // query rows per workgroup
+
+// V tiles of the wide kernel: 16-byte chunk c of row r at c ^ 2(r & 7), so the transposed V^T reads
+// (each 16-lane group: 4 rows x 2 adjacent chunks) of 32 lanes fall in 8 distinct 32-byte bank
+// groups (no bank conflicts, measured).
+__device__ __forceinline__ int vswz_wide(int row) { return 2 * (row & 7); }
+// K tiles of the wide kernel: chunk c of row r at c ^ kswz(r). With the narrow kernel's swz, the K
+// operand read (lane (li, lg): row li, chunk 4c + lg) had a 2-way bank conflict on every
+// ds_read_b128 (measured), though 16 consecutive lanes read 16 distinct chunks; the narrow
+// kernel's K read (lanes 0-31 at one chunk, 32-63 at the next) has none. Of the lane groupings
+// that fit both measurements, one serves lanes whose bits 2 and 4 agree (rows differing in bits 0,
+// 1, 3; chunks x and x ^ 2), another 8 lanes over half the banks (rows differing in bits 0 and 3;
+// chunks x and x ^ 2). kswz permutes the row mod 16 (16 rows at one chunk stay distinct); its bit 1
+// is row bit 2, constant in either group, so chunks x and x ^ 2 never meet; its bits 0, 2, 3 are
+// row bits 0, 3, 1, distinct over the rows of either group.
+__device__ __forceinline__ int kswz_wide(int row) {
+  return (row & 1) | (((row >> 2) & 1) << 1) | (((row >> 3) & 1) << 2) | (((row >> 1) & 1) << 3);
+}
+
+// Sum over the four lanes of one 16x16 column (lanes l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float col_sum(float x) { x += __shfl_xor(x, 16); return pair_sum(x); }
+__device__ __forceinline__ float col_max(float x) { x = __builtin_fmaxf(x, __shfl_xor(x, 16)); return pair_max(x); }
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_wide_kernel(const PrefillArgs<128> a) {
+  constexpr int D = 128, HALF = 64, CPR = 16, RPI = 4;
+  constexpr int NLDW = kBN / RPI / kWaves;  // direct loads per wave per tile (2)
+  constexpr bool kBif = MODE != kLocalOnly;
+  // Three K and three V tile buffers (96 KB), separate objects named statically in the code, so the
+  // compiler can tell a read of one from a direct load into another (it would otherwise wait for
+  // every load in flight before the read).
+  __shared__ __align__(16) uint16_t s_k0[kBN * D], s_k1[kBN * D], s_k2[kBN * D];
+  __shared__ __align__(16) uint16_t s_v0[kBN * D], s_v1[kBN * D], s_v2[kBN * D];
+  __shared__ uint32_t s_w[HALF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+
+  // ---- work item: XCD-aware remap of the linear workgroup id ----
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int per = nwg >> 3, rem = nwg & 7, xcd = bid & 7, slot = bid >> 3;
+  const int work = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int tile = a.n_tiles - 1 - work % a.n_tiles;  // longest rows first
+  const int bu = work / a.n_tiles;
+  const int unit = bu % a.n_units, b = bu / a.n_units;
+  const int Hg = a.Hq / a.Hkv;
+  const int upk = Hg / 4;
+  const int kvh = unit / upk;
+  const int head = kvh * Hg + (unit % upk) * 4 + (wave & 3);
+  const int i0 = a.q0 + tile * kWideBM;
+  const int iw = i0 + kWideCols * (wave >> 2);  // this wave's 48 query rows
+  const int L = a.L, w0 = a.w0, G = a.G;
+  const float qscale = a.scale_log2;
+
+  for (int t = tid; t < HALF; t += kThreads) s_w[t] = a.W[t];
+  __syncthreads();
+
+  const size_t q_row_stride = (size_t)a.Hq * D;
+  // Query operand (B of S^T = K Q^T) of column block cb, k-step c: lane (li, lg) holds query row
+  // iw + 16cb + li, d = 32c + 8lg .. +8, as given; with `rotate`, R(Delta_row) of it (pairs
+  // (d, d + 64) are registers c and c + 2 of the same lane), in fp32, rounded once to bf16.
+  auto load_q = [&](bool rotate, u32x4 (&dst)[3][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < 3; ++cb) {
+      const int qi = iw + 16 * cb + li;
+      const uint16_t* src = a.q + ((size_t)b * a.Lq + (qi - a.q0)) * q_row_stride + (size_t)head * D + 8 * lg;
+      u32x4 raw[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        raw[c] = u32x4{0, 0, 0, 0};
+        if (qi < L) raw[c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+      }
+      if (rotate) {
+        const int dq = correction_offset(qi < L ? qi : 0, G);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) rotate8(raw[c], raw[c + 2], dq, &s_w[32 * c + 8 * lg]);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[cb][c] = raw[c];
+    }
+  };
+
+  const int iw_last = min(iw + kWideCols - 1, L - 1);
+  const bool wave_live = iw <= L - 1;
+  const size_t kv_row_stride = (size_t)a.Hkv * D;
+  const size_t kv_off = (size_t)b * a.kv_cap * kv_row_stride + (size_t)kvh * D;
+  const size_t krot_off = (size_t)b * L * kv_row_stride + (size_t)kvh * D;  // workspace K' is [B, L, Hkv, D]
+  const uint16_t* kbase = a.k + kv_off;
+  const uint16_t* vbase = a.v + kv_off;
+
+  // ---- staging: as the narrow kernel, K tiles swizzled by kswz_wide, V tiles by vswz_wide ----
+  const int ld_row0 = RPI * NLDW * wave + lane / CPR;
+  const int ld_slot = lane % CPR;
+  uint32_t ld_off_k[NLDW], ld_off_v[NLDW];
+#pragma unroll
+  for (int n = 0; n < NLDW; ++n) {
+    const int row = ld_row0 + RPI * n;
+    ld_off_k[n] = (uint32_t)(row * (int)kv_row_stride + 8 * (ld_slot ^ kswz_wide(row))) * 2u;
+    ld_off_v[n] = (uint32_t)(row * (int)kv_row_stride + 8 * (ld_slot ^ vswz_wide(row))) * 2u;
+  }
+  auto stage = [&](const uint16_t* src, uint16_t* tile_lds, int j0, auto is_v) __attribute__((always_inline)) {
+    constexpr bool V = decltype(is_v)::value;
+    if (j0 + kBN <= L) {
+      const char* base = reinterpret_cast<const char*>(src + (size_t)j0 * kv_row_stride);
+#pragma unroll
+      for (int n = 0; n < NLDW; ++n)
+        load_lds16(base + (V ? ld_off_v[n] : ld_off_k[n]), tile_lds + (RPI * NLDW * wave + RPI * n) * D);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NLDW; ++n) {
+        const int row = ld_row0 + RPI * n;
+        const int j = min(j0 + row, L - 1);
+        const int sw = V ? vswz_wide(row) : kswz_wide(row);
+        load_lds16(src + (size_t)j * kv_row_stride + 8 * (ld_slot ^ sw), tile_lds + (RPI * NLDW * wave + RPI * n) * D);
+      }
+    }
+  };
+  const std::true_type is_v{};
+  const std::false_type is_k{};
+
+  // K operand (A of S^T = K Q^T) of k-step c: key row 16kb + li of the half tile, chunk 4c + lg;
+  // kswz depends on the row mod 16 only, so the 16-row block is an immediate offset.
+  int k_off[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    k_off[c] = li * D + 8 * ((4 * c + lg) ^ kswz_wide(li));
+    asm volatile("" : "+v"(k_off[c]));
+  }
+  // V^T operand (A of O^T += V^T P^T) of d block db: transposed reads of keys k0 = 4lg + li/4 and
+  // k0 + 16, d = 16db + 4(li%4) .. +4. Chunk (2db + h) ^ 2(k0 & 7) = 2(db ^ (k0 & 7)) + h, so the
+  // offset of block db is v_off ^ 16db (the pieces occupy disjoint bits).
+  const int tr_k0 = 4 * lg + (li >> 2), tr_lo = 4 * (li & 3);
+  int v_off = tr_k0 * D + 16 * (tr_k0 & 7) + 8 * (tr_lo >> 3) + (tr_lo & 7);
+  asm volatile("" : "+v"(v_off));
+
+  f32x4 o[8][3];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int cb = 0; cb < 3; ++cb) o[db][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float inv_qscale = 1.0f / qscale;
+  // m_run: a column's running max in log2 units (the same in its four lanes). A half tile's raw
+  // scores may reach (m_run + kSlack) / scale before the max is raised. l_run: the lane's share of
+  // the column's weight sum. Both passes weigh against the one running max, so the LSE merge of
+  // the local (W_A) and remote (W_B - W_C) weights is their sum: one running sum carries both.
+  float m_run[3], l_run[3];
+#pragma unroll
+  for (int cb = 0; cb < 3; ++cb) {
+    m_run[cb] = kNegBig;
+    l_run[cb] = 0.f;
+  }
+
+  // Index mask of a half tile (keys j0 + 32kbh + 16kb + 4lg + r, query rows iw + 16cb + li):
+  // kept iff lo_rel <= i - j, and i - j < w0 in the local pass.
+  auto mask = [&](f32x4 (&s)[2][3], int j0, int kbh, int lo_rel, bool local_pass) __attribute__((always_inline)) {
+    const int t0 = iw + li - j0 - 32 * kbh - 4 * lg;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + 16 * cb - 16 * kb - r;
+          const bool keep = (t >= lo_rel) && (!local_pass || t < w0);
+          if (!keep) s[kb][cb][r] = kNegBig;
+        }
+  };
+  // Phase 1: P^T of this half (bf16) against the stored max, its row sums added to the weight sum,
+  // the raw max fold and the rescale check. When some column's scores pass its limit, the column
+  // maxima are raised, the weight sum scaled by alpha and this half's P^T and sums recomputed
+  // against the new max; the caller scales O by alpha before this half's PV MFMAs. Returns whether
+  // it rose.
+  auto softmax = [&](const f32x4 (&s)[2][3], u32x4 (&p)[3], float (&alpha)[3]) __attribute__((always_inline)) {
+    float ps[3], mxl[3];
+#pragma unroll
+    for (int cb = 0; cb < 3; ++cb) {
+      ps[cb] = l_run[cb];
+      mxl[cb] = kMaskedMax;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int kb = w >> 1, r = 2 * (w & 1);
+        const uint32_t pk = pack_bf16x2(fast_exp2(__builtin_fmaf(s[kb][cb][r], qscale, -m_run[cb])),
+                                        fast_exp2(__builtin_fmaf(s[kb][cb][r + 1], qscale, -m_run[cb])));
+        p[cb][w] = pk;
+        ps[cb] = sum_bf16x2(pk, ps[cb]);
+        mxl[cb] = max3f(mxl[cb], s[kb][cb][r], s[kb][cb][r + 1]);
+      }
+    }
+    const float lim0 = (m_run[0] + kSlack) * inv_qscale, lim1 = (m_run[1] + kSlack) * inv_qscale;
+    const float lim2 = (m_run[2] + kSlack) * inv_qscale;
+    if (!wave_any(mxl[0] > lim0 || mxl[1] > lim1 || mxl[2] > lim2)) {
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb) l_run[cb] = ps[cb];
+      return false;
+    }
+#pragma unroll
+    for (int cb = 0; cb < 3; ++cb) {
+      const float mx_raw = col_max(mxl[cb]);
+      const float m_new = __builtin_fmaxf(m_run[cb], mx_raw * qscale);
+      alpha[cb] = fast_exp2(m_run[cb] - m_new);
+      m_run[cb] = m_new;
+      float acc = l_run[cb] * alpha[cb];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int kb = w >> 1, r = 2 * (w & 1);
+        const uint32_t pk = pack_bf16x2(fast_exp2(__builtin_fmaf(s[kb][cb][r], qscale, -m_new)),
+                                        fast_exp2(__builtin_fmaf(s[kb][cb][r + 1], qscale, -m_new)));
+        p[cb][w] = pk;
+        acc = sum_bf16x2(pk, acc);
+      }
+      l_run[cb] = acc;
+    }
+    return true;
+  };
+  // Phase 2 in 16 slots of three MFMAs (one per column block): slots 0-7 the PV MFMAs of this half
+  // (V rows 32 hv .. of vs, d block = slot, P^T p), slots 8-15 the score MFMAs of the next half (K
+  // rows 32 hk .. of ks into s; k-step = slot - 8). The LDS operand of a slot is read AHEAD slots
+  // before it; sched_barrier keeps the slot order.
+  auto phase2 = [&](const uint16_t* vs, int hv, const u32x4 (&p)[3], const uint16_t* ks, int hk,
+                    const u32x4 (&qa)[3][4], f32x4 (&s)[2][3]) __attribute__((always_inline)) {
+    const uint16_t* khalf = ks + 32 * hk * D;
+    const uint16_t* vhalf = vs + 32 * hv * D;
+    auto read_op = [&](int m) __attribute__((always_inline)) {
+      if (m >= 8) {
+        const int kb = (m - 8) >> 2, c = (m - 8) & 3;
+        return *reinterpret_cast<const u32x4*>(khalf + 16 * kb * D + k_off[c]);
+      }
+      const uint16_t* r = vhalf + (v_off ^ (16 * m));
+      const u32x2 v0 = read_tr(r), v1 = read_tr(r + 16 * D);
+      return u32x4{v0[0], v0[1], v1[0], v1[1]};
+    };
+    constexpr int AHEAD = 4;
+    u32x4 op[16];
+#pragma unroll
+    for (int m = 0; m < AHEAD; ++m) op[m] = read_op(m);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (m + AHEAD < 16) op[m + AHEAD] = read_op(m + AHEAD);
+      if (m < 8) {
+#pragma unroll
+        for (int cb = 0; cb < 3; ++cb) o[m][cb] = mfma16(op[m], p[cb], o[m][cb]);
+      } else {
+        const int kb = (m - 8) >> 2, c = (m - 8) & 3;
+#pragma unroll
+        for (int cb = 0; cb < 3; ++cb) s[kb][cb] = mfma16(op[m], qa[cb][c], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb][cb]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Score MFMAs alone (the first half of a pass).
+  auto scores = [&](const uint16_t* ks, const u32x4 (&qa)[3][4], f32x4 (&s)[2][3]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int kb = st >> 2, c = st & 3;
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(ks + 16 * kb * D + k_off[c]);
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb) s[kb][cb] = mfma16(ka, qa[cb][c], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb][cb]);
+    }
+  };
+
+  // One pass over n tiles kt = kt_first, kt_first-1, ... (tile t holds keys j0(t) .. +63). Tile t:
+  //   barrier t (for t > 0); loads of K_{t+2} and V_{t+1};
+  //   half (t,0): mask, softmax; pv(t,0) [V_t] beside scores(t,1) [K_t];
+  //   half (t,1): mask, softmax; pv(t,1) [V_t] beside scores(t+1,0) [K_{t+1}].
+  // K and V tile t sit in buffers t % 3. A load issued after barrier t targets a buffer last read
+  // before barrier t (K_{t-1}: scores(t-1,1); V_{t-2}: pv(t-2,1)) and is waited before barrier
+  // t+1, which precedes its first read (scores(t+2,0) at the end of tile t+1; pv(t+1,0)). The loop
+  // is unrolled by three so every buffer is named statically.
+  auto run_pass = [&](int kt_first, int n, const u32x4 (&qa)[3][4], const uint16_t* ksrc, bool local_pass, int lo_rel)
+                      __attribute__((always_inline)) {
+    auto j0_of = [&](int t) { return (kt_first - t) * kBN; };
+    auto needs_mask = [&](int t) __attribute__((always_inline)) {
+      const int j0 = j0_of(t);
+      const int w_max = iw_last - j0, w_min = iw - (j0 + kBN - 1);
+      const bool masked = local_pass ? !(w_min >= 0 && w_max < w0) : (w_min < w0);
+      const bool active = wave_live && (local_pass ? (w_max >= 0 && w_min < w0) : (w_max >= w0));
+      return masked || !active;
+    };
+    stage(ksrc, s_k0, j0_of(0), is_k);
+    if (n > 1) stage(ksrc, s_k1, j0_of(1), is_k);
+    stage(vbase, s_v0, j0_of(0), is_v);
+    wait_loads();
+    __syncthreads();
+    f32x4 s[2][3];
+    scores(s_k0, qa, s);
+    auto half = [&](int t, int hh, bool msk, u32x4 (&p)[3]) __attribute__((always_inline)) {
+      if (msk) mask(s, j0_of(t), hh, lo_rel, local_pass);
+      float alpha[3];
+      if (softmax(s, p, alpha)) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int cb = 0; cb < 3; ++cb) o[db][cb] *= alpha[cb];
+      }
+    };
+    // kt, vt: buffers of tile t; kn, vn: of tile t+1; kf: of tile t+2.
+    auto tile = [&](int t, const uint16_t* kt, const uint16_t* kn, uint16_t* kf, const uint16_t* vt, uint16_t* vn)
+                    __attribute__((always_inline)) {
+      if (t > 0) {
+        wait_loads();
+        __syncthreads();
+      }
+      if (t + 2 < n) stage(ksrc, kf, j0_of(t + 2), is_k);
+      if (t + 1 < n) stage(vbase, vn, j0_of(t + 1), is_v);
+      const bool msk = needs_mask(t);
+      u32x4 p[3];
+      half(t, 0, msk, p);
+      phase2(vt, 0, p, kt, 1, qa, s);
+      half(t, 1, msk, p);
+      // In the last tile these scores read a buffer no tile needs and are not used; a branch
+      // around them would carry O through two code paths.
+      phase2(vt, 1, p, kn, 0, qa, s);
+    };
+    for (int t = 0; t < n; t += 3) {
+      tile(t, s_k0, s_k1, s_k2, s_v0, s_v1);
+      if (t + 1 < n) tile(t + 1, s_k1, s_k2, s_k0, s_v1, s_v2);
+      if (t + 2 < n) tile(t + 2, s_k2, s_k0, s_k1, s_v2, s_v0);
+    }
+    __syncthreads();  // the next pass's prologue refills the buffers
+  };
+
+  const int i_last = min(i0 + kWideBM, L) - 1;
+  // Pass A: local pairs, tiles n_kt-1 down to kt_lo (base vectors). Pass R: remote pairs, tiles
+  // kt_hi-1 down to 0 (rotated queries, keys rotated in the workspace). One loop body serves both.
+  const int n_kt = i_last / kBN + 1;
+  const int kt_lo = max(0, i0 - w0 + 1) / kBN;
+  const int kt_hi = kBif ? ((i_last >= w0) ? (i_last - w0) / kBN + 1 : 0) : 0;
+  u32x4 q[3][4];
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool local_pass = pass == 0;
+    const int n = local_pass ? (w0 > 0 ? n_kt - kt_lo : 0) : kt_hi;
+    if (n <= 0) continue;
+    load_q(!local_pass, q);
+    run_pass(local_pass ? n_kt - 1 : kt_hi - 1, n, q, local_pass ? kbase : a.krot + krot_off, local_pass,
+             local_pass ? 0 : w0);
+  }
+
+  // ---- epilogue: per column, LSE merge of the local and remote weights, normalise, store ----
+#pragma unroll
+  for (int cb = 0; cb < 3; ++cb) {
+    const float den = col_sum(l_run[cb]);  // W_A + (W_B - W_C), relative to 2^m_run
+    const float inv = 1.0f / den;
+    const int qi = iw + 16 * cb + li;
+    if (qi < L) {
+      const size_t orow = ((size_t)b * a.Lq + (qi - a.q0)) * q_row_stride + (size_t)head * D + 4 * lg;
+      bool done = false;
+      if constexpr (MODE == kLocalOnly) {
+        if (a.o32 != nullptr) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db)
+            *reinterpret_cast<f32x4*>(a.o32 + orow + 16 * db) = o[db][cb] * inv;
+          done = true;
+        }
+      }
+      if (!done) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          u32x2 out;
+          out[0] = pack_bf16x2(o[db][cb][0] * inv, o[db][cb][1] * inv);
+          out[1] = pack_bf16x2(o[db][cb][2] * inv, o[db][cb][3] * inv);
+          *reinterpret_cast<u32x2*>(a.o + orow + 16 * db) = out;
+        }
+      }
+      if (a.lse != nullptr && lg == 0)
+        a.lse[((size_t)b * a.Hq + head) * a.Lq + (qi - a.q0)] = (m_run[cb] + __log2f(den)) * 0.69314718055994531f;
+    }
+  }
+}
+
 // K' = R(Delta_j) K~ for every key row j < L (prerotated mode): one thread per 8 rotation pairs.
 // Reads k with kv_cap rows per batch, writes the compact [B, L, Hkv, D] workspace.
 template <int D>
@@ -588,12 +980,33 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
   a.n_units = p.n_q_heads / a.hpw;
   a.scale_log2 = p.scale_log2;
   for (int i = 0; i < D / 2; ++i) a.W[i] = p.W[i];
+  // D = 128 with four query heads per workgroup, all local or keys rotated into the workspace: the
+  // wide-wave kernel (48 query rows per wave, BM = 96), unless the grid is short and even. Query
+  // rows at the end of a much longer cache give every workgroup the same long key range, and a
+  // grid of few such workgroups finishes in whole rounds over the CUs: there the narrow kernel's
+  // shorter workgroups round up to less time (4096 rows after 126976 keys, Qwen3-8B heads: 344
+  // wide workgroups, 7.5 against 10.8 ms). A grid of 2048 or more, or rows starting no later
+  // than their own count (causal work varying per tile, longest first), keeps the wide kernel.
+  bool wide = false;
+  if constexpr (D == 128) {
+    if (a.hpw == 4 && (p.w0 >= p.L || p.local_only || p.krot != nullptr)) {
+      const long long nwg_wide = (long long)p.batch * a.n_units * ((p.Lq + kWideBM - 1) / kWideBM);
+      wide = (p.L - p.Lq) <= p.Lq || nwg_wide >= 2048;
+    }
+  }
+  if (wide) a.n_tiles = (p.Lq + kWideBM - 1) / kWideBM;
   const long long nwg = (long long)p.batch * a.n_units * a.n_tiles;
   if (nwg <= 0 || nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   // With every pair local (w0 == L, which the host also sets for G == 1) there is no remote
   // key: plain causal attention with no rotation at all. local_only asks for that pass alone
   // with w0 < L: plain sliding-window attention.
   if (p.w0 >= p.L || p.local_only) {
+    if constexpr (D == 128) {
+      if (wide) {
+        hipLaunchKernelGGL((prefill_wide_kernel<kLocalOnly>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((prefill_kernel<D, kLocalOnly>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   } else if (p.krot != nullptr) {
     const long long rows = (long long)p.batch * p.L * p.n_kv_heads;
@@ -602,6 +1015,12 @@ static hipError_t launch_prefill_d(const PrefillLaunch& p, hipStream_t stream) {
                        static_cast<uint16_t*>(p.krot), rows, p.n_kv_heads, p.L, p.kv_cap, p.G, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (D == 128) {
+      if (wide) {
+        hipLaunchKernelGGL((prefill_wide_kernel<kPrerotated>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((prefill_kernel<D, kPrerotated>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL((prefill_kernel<D, kFused>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
