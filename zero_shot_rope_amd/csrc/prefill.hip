@@ -540,12 +540,15 @@ void prefill_kernel(const PrefillArgs<D> a) {
 // head, as three 16-column blocks of v_mfma_f32_16x16x32_bf16, so every K and V operand read from
 // LDS feeds three MFMAs: 2/3 of the LDS bytes per unit of matrix work of the 32-row wave above.
 // Measured at the 128K layer shape, the narrow kernel keeps the MFMA pipe 63% busy at a clock the
-// power budget holds near 1.76 GHz; this one 50% busy at 2.26 GHz, and finishes 2-3% sooner.
+// power budget holds near 1.76-1.82 GHz; this one 54% busy at 2.19 GHz, and finishes 3-4% sooner.
+// The clock falls as the MFMA pipe gets busier: the lower LDS traffic is what buys the time.
 // 8 waves = 4 heads x 2 row groups: BM = 96 query rows per workgroup. Registers do not allow the
 // three-stage half step of the narrow kernel; a half step here is two phases:
 //   1. softmax of this half's scores (P, exponentials against the stored max, row sums, max fold,
 //      rescale check; a raised max scales O and the weight sum first);
 //   2. this half's PV MFMAs, then the next half's score MFMAs.
+// The two waves of a SIMD run these phases out of step (one row group does a tile's first softmax
+// before the barrier), so one wave's softmax runs beside the other's MFMAs.
 // With no lag between scores and PV, the keys of tile t+1 are read (its first score half) before
 // the barrier of tile t+1, so K and V are triple-buffered: one barrier per tile still covers the
 // direct loads, each issued a tile before the barrier that publishes it.
@@ -673,6 +676,25 @@ void prefill_wide_kernel(const PrefillArgs<128> a) {
         load_lds16(src + (size_t)j * kv_row_stride + 8 * (ld_slot ^ sw), tile_lds + (RPI * NLDW * wave + RPI * n) * D);
       }
     }
+  };
+  // In-loop loads: every tile after a pass's first one lies below row L - 1 (tiles go from the
+  // highest keys down, and only the first can be partial), so no clamping. The lane offsets are
+  // recomputed at each use from a lane id hidden from the optimiser (a few VALU per tile), so
+  // they hold no registers across the tile loop, and the load takes the scalar base plus a
+  // 32-bit lane offset.
+  auto stage_full = [&](const uint16_t* src, uint16_t* tile_lds, int j0, auto is_v) __attribute__((always_inline)) {
+    constexpr bool V = decltype(is_v)::value;
+    const char* base = reinterpret_cast<const char*>(src + (size_t)j0 * kv_row_stride);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    uint32_t off[NLDW];
+#pragma unroll
+    for (int n = 0; n < NLDW; ++n) {
+      const int row = RPI * NLDW * wave + (ln >> 4) + RPI * n, slot = ln & 15;
+      off[n] = (uint32_t)(row * (int)kv_row_stride + 8 * (slot ^ (V ? vswz_wide(row) : kswz_wide(row)))) * 2u;
+    }
+#pragma unroll
+    for (int n = 0; n < NLDW; ++n) load_lds16(base + off[n], tile_lds + (RPI * NLDW * wave + RPI * n) * D);
   };
   const std::true_type is_v{};
   const std::false_type is_k{};
@@ -843,8 +865,17 @@ void prefill_wide_kernel(const PrefillArgs<128> a) {
     __syncthreads();
     f32x4 s[2][3];
     scores(s_k0, qa, s);
+    // Softmax of half (t, hh). Past the last tile (t == n) every score is masked: the scores there
+    // came from a buffer no tile needs, and a fully masked half adds no weight.
     auto half = [&](int t, int hh, bool msk, u32x4 (&p)[3]) __attribute__((always_inline)) {
-      if (msk) mask(s, j0_of(t), hh, lo_rel, local_pass);
+      if (t >= n) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int cb = 0; cb < 3; ++cb) s[kb][cb] = f32x4{kNegBig, kNegBig, kNegBig, kNegBig};
+      } else if (msk) {
+        mask(s, j0_of(t), hh, lo_rel, local_pass);
+      }
       float alpha[3];
       if (softmax(s, p, alpha)) {
 #pragma unroll
@@ -853,6 +884,14 @@ void prefill_wide_kernel(const PrefillArgs<128> a) {
           for (int cb = 0; cb < 3; ++cb) o[db][cb] *= alpha[cb];
       }
     };
+    // The two waves on a SIMD (waves w and w + 4: one per row group) run out of phase. The first
+    // row group leads each tile with the softmax of its first half; the second does that softmax
+    // at the end of the previous tile, before the barrier, so after the barrier it starts with its
+    // MFMAs. From there, each wave's softmax VALU runs beside the other's MFMA phase. The softmax
+    // reads no LDS, so the buffer protocol is unchanged.
+    const bool lead = wave < 4;
+    u32x4 p[3];
+    if (!lead) half(0, 0, needs_mask(0), p);
     // kt, vt: buffers of tile t; kn, vn: of tile t+1; kf: of tile t+2.
     auto tile = [&](int t, const uint16_t* kt, const uint16_t* kn, uint16_t* kf, const uint16_t* vt, uint16_t* vn)
                     __attribute__((always_inline)) {
@@ -860,16 +899,16 @@ void prefill_wide_kernel(const PrefillArgs<128> a) {
         wait_loads();
         __syncthreads();
       }
-      if (t + 2 < n) stage(ksrc, kf, j0_of(t + 2), is_k);
-      if (t + 1 < n) stage(vbase, vn, j0_of(t + 1), is_v);
+      if (t + 2 < n) stage_full(ksrc, kf, j0_of(t + 2), is_k);
+      if (t + 1 < n) stage_full(vbase, vn, j0_of(t + 1), is_v);
       const bool msk = needs_mask(t);
-      u32x4 p[3];
-      half(t, 0, msk, p);
+      if (lead) half(t, 0, msk, p);
       phase2(vt, 0, p, kt, 1, qa, s);
       half(t, 1, msk, p);
       // In the last tile these scores read a buffer no tile needs and are not used; a branch
       // around them would carry O through two code paths.
       phase2(vt, 1, p, kn, 0, qa, s);
+      if (!lead) half(t + 1, 0, t + 1 < n && needs_mask(t + 1), p);
     };
     for (int t = 0; t < n; t += 3) {
       tile(t, s_k0, s_k1, s_k2, s_v0, s_v1);
