@@ -197,7 +197,8 @@ def sample_rows(L, w0, G, seed, n_random=24):
 
 def dense_rows(L, w0, G, seed, tile=64):
     """One random row in every `tile`-row query tile (so every workgroup of the prefill grid has
-    a compared row), plus the first and last 64 rows, rows w0-1..w0+1 and 2w0-1..2w0+1 (the
+    a compared row: the narrow kernel's tiles are 64 rows, and each 96-row tile of the wide
+    kernel, starting at a multiple of 96, holds a whole 64-row tile), plus the first and last 64 rows, rows w0-1..w0+1 and 2w0-1..2w0+1 (the
     first remote pairs), and rows at +-1 of multiples of tile*G (a tile edge that is also a
     multiple of G) at a quarter, half and three quarters of L."""
     rng = np.random.default_rng(seed)
