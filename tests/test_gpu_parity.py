@@ -291,6 +291,11 @@ SMALL_CHUNK = [
     (1, 500, 4, 1, 128, 1000, 50, 1e6, [(100, 400)]),                                # G = 1
     (1, 600, 4, 4, 64, 64, 0, 1e4, [(200, 300)]),                                    # w0 = 0
     (1, 800, 8, 1, 128, 64, 700, 1e4, [(600, 200)]),                                 # 8:1 GQA, wide band
+    # Chunks that start mid-sequence and no later than their own length, with four query heads
+    # per KV head at D = 128: the wide-wave prefill kernel, its 96-row tiles starting off any
+    # 64-key boundary.
+    (1, 900, 32, 8, 128, 200, 110, 1e6, [(300, 600), (437, 463)]),                  # Qwen3-8B heads, G 5
+    (2, 700, 16, 2, 128, 150, 90, 1e4, [(250, 450), (333, 367)]),                   # 8:1 GQA, batch 2
 ]
 
 
