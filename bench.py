@@ -71,7 +71,7 @@ def parse():
 # otherwise the kernel changed since the counters were taken and the traffic is reported as null.
 MEASURED_TRAFFIC = {
     # rotate_keys_kernel + prefill_wide_kernel<prerotated> at the 128K Qwen3-8B shape.
-    "prefill": {"sources": "c9aa436cff371de2", "fetch_bytes": 25637.42e6, "write_bytes": 2035.98e6},
+    "prefill": {"sources": "704fbfb1272a411b", "fetch_bytes": 25643.87e6, "write_bytes": 2058.42e6},
     # decode_split_kernel + decode_reduce_kernel, mean over the 512 steps (L 98001..98512).
     "decode": {"sources": "f10c98a5d45fbe6d", "fetch_bytes": 407.06e6, "write_bytes": 4.33e6},
 }

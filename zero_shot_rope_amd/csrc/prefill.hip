@@ -540,8 +540,8 @@ void prefill_kernel(const PrefillArgs<D> a) {
 // head, as three 16-column blocks of v_mfma_f32_16x16x32_bf16, so every K and V operand read from
 // LDS feeds three MFMAs: 2/3 of the LDS bytes per unit of matrix work of the 32-row wave above.
 // Measured at the 128K layer shape, the narrow kernel keeps the MFMA pipe 63% busy at a clock the
-// power budget holds near 1.76-1.82 GHz; this one 54% busy at 2.19 GHz, and finishes 3-4% sooner.
-// The clock falls as the MFMA pipe gets busier: the lower LDS traffic is what buys the time.
+// power budget holds near 1.8 GHz; this one about 55% busy at 2.2 GHz, and finishes 4-5% sooner.
+// The clock falls as the MFMA pipe gets busier: the lower LDS and VALU work is what buys the time.
 // 8 waves = 4 heads x 2 row groups: BM = 96 query rows per workgroup. Registers do not allow the
 // three-stage half step of the narrow kernel; a half step here is two phases:
 //   1. softmax of this half's scores (P, exponentials against the stored max, row sums, max fold,
@@ -593,6 +593,8 @@ void prefill_wide_kernel(const PrefillArgs<128> a) {
   __shared__ __align__(16) uint16_t s_k0[kBN * D], s_k1[kBN * D], s_k2[kBN * D];
   __shared__ __align__(16) uint16_t s_v0[kBN * D], s_v1[kBN * D], s_v2[kBN * D];
   __shared__ uint32_t s_w[HALF];
+  // Per lane, the byte offsets of its direct loads: K rows n = 0, 1, then V rows n = 0, 1.
+  __shared__ __align__(16) uint32_t s_ldoff[kThreads * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -660,6 +662,7 @@ void prefill_wide_kernel(const PrefillArgs<128> a) {
     ld_off_k[n] = (uint32_t)(row * (int)kv_row_stride + 8 * (ld_slot ^ kswz_wide(row))) * 2u;
     ld_off_v[n] = (uint32_t)(row * (int)kv_row_stride + 8 * (ld_slot ^ vswz_wide(row))) * 2u;
   }
+  *reinterpret_cast<u32x4*>(&s_ldoff[4 * tid]) = u32x4{ld_off_k[0], ld_off_k[1], ld_off_v[0], ld_off_v[1]};
   auto stage = [&](const uint16_t* src, uint16_t* tile_lds, int j0, auto is_v) __attribute__((always_inline)) {
     constexpr bool V = decltype(is_v)::value;
     if (j0 + kBN <= L) {
@@ -678,23 +681,17 @@ void prefill_wide_kernel(const PrefillArgs<128> a) {
     }
   };
   // In-loop loads: every tile after a pass's first one lies below row L - 1 (tiles go from the
-  // highest keys down, and only the first can be partial), so no clamping. The lane offsets are
-  // recomputed at each use from a lane id hidden from the optimiser (a few VALU per tile), so
-  // they hold no registers across the tile loop, and the load takes the scalar base plus a
-  // 32-bit lane offset.
+  // highest keys down, and only the first can be partial), so no clamping. The lane offsets come
+  // from the lane's own entry of an LDS table, one ds_read_b128 per use, so they hold no
+  // registers across the tile loop (kept in registers they spilled, and each reload's wait held
+  // one direct load behind the one before it), and the load takes the scalar base plus a 32-bit
+  // lane offset. Recomputing them instead cost 9% more VALU instructions and 1-2% of the time.
   auto stage_full = [&](const uint16_t* src, uint16_t* tile_lds, int j0, auto is_v) __attribute__((always_inline)) {
     constexpr bool V = decltype(is_v)::value;
     const char* base = reinterpret_cast<const char*>(src + (size_t)j0 * kv_row_stride);
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    uint32_t off[NLDW];
+    const u32x4 offs = *reinterpret_cast<const u32x4*>(&s_ldoff[4 * tid]);
 #pragma unroll
-    for (int n = 0; n < NLDW; ++n) {
-      const int row = RPI * NLDW * wave + (ln >> 4) + RPI * n, slot = ln & 15;
-      off[n] = (uint32_t)(row * (int)kv_row_stride + 8 * (slot ^ (V ? vswz_wide(row) : kswz_wide(row)))) * 2u;
-    }
-#pragma unroll
-    for (int n = 0; n < NLDW; ++n) load_lds16(base + off[n], tile_lds + (RPI * NLDW * wave + RPI * n) * D);
+    for (int n = 0; n < NLDW; ++n) load_lds16(base + offs[(V ? 2 : 0) + n], tile_lds + (RPI * NLDW * wave + RPI * n) * D);
   };
   const std::true_type is_v{};
   const std::false_type is_k{};
