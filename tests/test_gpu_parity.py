@@ -913,6 +913,47 @@ def test_random_sweep(i):
                                               theta=theta)
     compare(o, rs_o, "decode step")
     assert np.max(np.abs(lse - rs_lse)) <= LSE_ABS
+def _wide_case(i):
+    """D = 128 with 4, 8 or 16 query heads per KV head: the shapes the wide-wave prefill kernel
+    serves (keys rotated, plain passes, chunks that start no later than their length)."""
+    rng = np.random.default_rng(50000 + i)
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([4, 8, 16]))
+    if Hq > 16:
+        Hq = Hkv * 4
+    B = int(rng.choice([1, 1, 2]))
+    L = int(rng.integers(1, 900))
+    wp = int(rng.integers(1, 400))
+    w0 = int(rng.choice([0, 1, int(rng.integers(0, 300)), 5000]))
+    theta = float(rng.choice([1e4, 1e6]))
+    return B, L, Hq, Hkv, wp, w0, theta
+
+
+WIDE_SWEEP = [_wide_case(i) for i in range(48)]
+
+
+@pytest.mark.parametrize("i", range(len(WIDE_SWEEP)), ids=[f"w{i}-B{c[0]}L{c[1]}H{c[2]}-{c[3]}wp{c[4]}w{c[5]}"
+                                                          for i, c in enumerate(WIDE_SWEEP)])
+def test_wide_prefill_sweep(i):
+    B, L, Hq, Hkv, wp, w0, theta = WIDE_SWEEP[i]
+    say(f"wide sweep {i}: B={B} L={L} Hq={Hq} Hkv={Hkv} wp={wp} w0={w0} theta={theta:g} G={group_size(L, wp)}")
+    bits = W.random_case(60000 + i, B, L, Hq, Hkv, 128)
+    qf, kf, vf = f64(bits["q"]), f64(bits["k"]), f64(bits["v"])
+    ref_o, ref_lse = bifocal_attention(qf, kf, vf, w0=w0, w_pretrained=wp, theta=theta)
+    o, lse = run_prefill(bits, w0, wp, theta, "prerotated")
+    compare(o, ref_o, "prefill prerotated")
+    assert np.max(np.abs(lse - ref_lse)) <= LSE_ABS
+    u_o, u_lse = three_pass_attention(qf, kf, vf, w0=w0, w_pretrained=wp, theta=theta)
+    o, lse = run_prefill(bits, w0, wp, theta, "unfused")
+    compare(o, u_o, "prefill unfused")
+    assert np.max(np.abs(lse - u_lse)) <= LSE_ABS
+    q_len = max(1, (2 * L) // 3)
+    q_off = L - q_len
+    o, lse = run_chunk(bits["q"][:, q_off:], bits["k"], bits["v"], q_off, w0, wp, theta, "prerotated")
+    compare(o, ref_o[:, q_off:], f"chunk offset={q_off}")
+    assert np.max(np.abs(lse - ref_lse[:, :, q_off:])) <= LSE_ABS
+
+
 
 
 def test_calls_are_deterministic():
